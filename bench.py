@@ -1,0 +1,318 @@
+"""Benchmark of the paged-KV Gemma attention hot path on one MI355X.
+
+A step is one pass of the path over one batch: ga_kv_cache_write of the batch's new tokens
+(norm + RoPE + scatter), then the attention call over the paged cache.  The headline line
+measures the bf16 soft-capped decode workload (32 sequences, lengths U[512, 4096], 8 query /
+4 kv heads, head size 256, cap 50, scale 1/16); the same JSON line also carries the chunked
+prefill workload (4 x 2048 new tokens after 6144 cached, 5 sliding + 1 global layer) and the
+two other decode workloads, each with its own roofline fraction.
+
+value = algorithmic KV bytes read by decode attention per step / wall time per step (GB/s).
+Inputs are resident in HBM; the caches are rotated over several copies so that the 256 MB
+last-level cache cannot hold a step's working set.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import paged_kv_cache_write_amd as ga  # noqa: E402
+import workloads as wl  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
+BS = wl.BLOCK_SIZE
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def params(spec):
+    return ga.layer_params(spec.dtype, spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
+                           window=spec.window, scale=spec.scale, softcap=spec.softcap,
+                           k_eq_v=spec.k_eq_v, rope_theta=spec.rope_theta, rms_eps=spec.rms_eps)
+
+
+def i32(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+
+# ----------------------------------------------------------------------------- work models ---
+
+def decode_bytes(spec, lens):
+    """Algorithmic bytes of one decode attention call: the visible keys' K (and V) rows, the
+    query, the output and the block-table entries read."""
+    e = 2 if spec.dtype == "bf16" else 4
+    kv_mult = 1 if spec.k_eq_v else 2
+    total = 0
+    for L in lens:
+        keys = min(int(L), spec.window) if spec.window > 0 else int(L)
+        lo = int(L) - keys
+        pages = (int(L) - 1) // BS - lo // BS + 1
+        total += keys * spec.num_kv_heads * spec.head_dim * e * kv_mult
+        total += pages * 4 * spec.num_kv_heads
+    total += 2 * len(lens) * spec.num_q_heads * spec.head_dim * e
+    return total
+
+
+def prefill_flops(spec, lens, news):
+    """4*D flop per visible (query, key, query head) triple (QK^T and PV)."""
+    total = 0
+    for L, n in zip(lens, news):
+        past = int(L) - int(n)
+        t = past + np.arange(int(n), dtype=np.int64)
+        if spec.window > 0:
+            vis = np.minimum(t + 1, spec.window)
+        else:
+            vis = t + 1
+        total += int(vis.sum())
+    return total * spec.num_q_heads * 4 * spec.head_dim
+
+
+# ----------------------------------------------------------------------------- set-up ---------
+
+class DecodeBench:
+    """Caches for one decode workload, the past written by the library, `copies` copies."""
+
+    def __init__(self, name, copies, dev, seed=0):
+        specs, pb = wl.workload(name)
+        self.name, self.spec, self.pb, self.dev = name, specs[0], pb, dev
+        s = self.spec
+        self.p = params(s)
+        lens = pb.context_lens
+        past = lens - 1
+        self.w = [None if x is None else x.to(dev) for x in wl.norm_weights(s, seed)]
+        self.bt = i32(pb.block_table, dev)
+        self.cl = i32(lens, dev)
+        self.cu1 = i32(np.arange(pb.batch + 1), dev)
+        kc, vc = wl.empty_caches(s, pb.num_blocks, dev)
+        # the past, written by the library in chunks (not timed)
+        self._write_past(kc, vc, past, seed)
+        self.kcs, self.vcs = [kc], [vc]
+        for _ in range(copies - 1):
+            self.kcs.append(kc.clone())
+            self.vcs.append(None if vc is None else vc.clone())
+        q, k, v = wl.raw_qkv(s, pb.batch, seed + 1, device=dev)
+        self.q, self.k, self.v = q, k, v
+        self.out = torch.empty(pb.batch, s.num_q_heads, s.head_dim, dtype=s.torch_dtype,
+                               device=dev)
+        self.max_len = int(lens.max())
+        self.ws = ga.decode_workspace(self.p, pb.batch, self.max_len, dev)
+        self.bytes = decode_bytes(s, lens)
+        ga.check_metadata_host(self.p, torch.from_numpy(np.arange(pb.batch + 1, dtype=np.int32)),
+                               torch.from_numpy(lens), torch.from_numpy(pb.block_table),
+                               pb.num_blocks)
+
+    def _write_past(self, kc, vc, past, seed):
+        s, dev = self.spec, self.dev
+        B = len(past)
+        chunk = 4096
+        start = np.zeros(B, np.int64)
+        while (start < past).any():
+            n = np.minimum(past - start, chunk).astype(np.int32)
+            cl = (start + n).astype(np.int32)
+            cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+            T = int(cu[-1])
+            _, k, v = wl.raw_qkv(s, T, seed + 1000 + int(start.max()), device=dev)
+            ga.kv_cache_write(self.p, None, k, v, *self.w, i32(cu, dev), i32(cl, dev), self.bt,
+                              kc, vc)
+            start = start + n
+        torch.cuda.synchronize()
+
+    def write(self, i):
+        c = i % len(self.kcs)
+        ga.kv_cache_write(self.p, self.q, self.k, self.v, *self.w, self.cu1, self.cl, self.bt,
+                          self.kcs[c], self.vcs[c])
+
+    def attend(self, i):
+        c = i % len(self.kcs)
+        ga.attn_decode(self.p, self.q, self.kcs[c], self.vcs[c], self.bt, self.cl, self.max_len,
+                       out=self.out, workspace=self.ws)
+
+
+class PrefillBench:
+    """The 6-layer chunked-prefill stack: per layer a write of the 4 x 2048 chunk + prefill."""
+
+    def __init__(self, dev, seed=0):
+        specs, pb = wl.workload("chunked_prefill_bf16")
+        self.specs, self.pb, self.dev = specs, pb, dev
+        self.layers = []
+        lens, news = pb.context_lens, pb.n_new
+        past = lens - news
+        self.bt = i32(pb.block_table, dev)
+        self.cu = i32(pb.cu_seqlens, dev)
+        self.cl = i32(lens, dev)
+        cu_past = np.concatenate([[0], np.cumsum(past)]).astype(np.int32)
+        for li, s in enumerate(specs):
+            p = params(s)
+            w = [None if x is None else x.to(dev) for x in wl.norm_weights(s, 50 + li)]
+            kc, vc = wl.empty_caches(s, pb.num_blocks, dev)
+            _, kp, vp = wl.raw_qkv(s, int(cu_past[-1]), 500 + li, device=dev)
+            ga.kv_cache_write(p, None, kp, vp, *w, i32(cu_past, dev), i32(past, dev), self.bt,
+                              kc, vc)
+            q, k, v = wl.raw_qkv(s, pb.total_new, 600 + li, device=dev)
+            out = torch.empty_like(q)
+            self.layers.append(dict(p=p, w=w, kc=kc, vc=vc, q=q, k=k, v=v, out=out, spec=s))
+            del kp, vp
+        torch.cuda.synchronize()
+        self.flops = sum(prefill_flops(s, lens, news) for s in specs)
+        self.max_q = int(news.max())
+
+    def write(self, li):
+        L = self.layers[li]
+        ga.kv_cache_write(L["p"], L["q"], L["k"], L["v"], *L["w"], self.cu, self.cl, self.bt,
+                          L["kc"], L["vc"])
+
+    def attend(self, li):
+        L = self.layers[li]
+        ga.attn_prefill(L["p"], L["q"], self.cu, L["kc"], L["vc"], self.bt, self.cl, self.max_q,
+                        out=L["out"])
+
+
+# ----------------------------------------------------------------------------- timing ---------
+
+def time_steps(write, attend, steps, warmup, inner=1):
+    """Warm up, then time `steps` steps; every step is `inner` x (write, attend).  Returns
+    (wall ms per step, mean event ms of the writes, mean event ms of the attention calls)."""
+    for i in range(warmup):
+        for j in range(inner):
+            write(j)
+            attend(j)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps * inner)]
+    t0 = time.perf_counter()
+    n = 0
+    for i in range(steps):
+        for j in range(inner):
+            e = ev[n]
+            e[0].record()
+            write(i * inner + j if inner == 1 else j)
+            e[1].record()
+            attend(i * inner + j if inner == 1 else j)
+            e[2].record()
+            n += 1
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    w = np.mean([e[0].elapsed_time(e[1]) for e in ev])
+    a = np.mean([e[1].elapsed_time(e[2]) for e in ev])
+    return wall, float(w), float(a)
+
+
+def cpu_baseline_decode(db: DecodeBench, budget_s: float):
+    """The oracle on the host cores, over the same decode batch (the cache copied back)."""
+    import oracle
+    s, pb = db.spec, db.pb
+    kc = wl.to_numpy_bits(db.kcs[0])
+    vc = None if db.vcs[0] is None else wl.to_numpy_bits(db.vcs[0])
+    q = wl.to_numpy_bits(db.q)
+    code = oracle.BF16 if s.dtype == "bf16" else oracle.FP32
+    runs, t_total = 0, 0.0
+    while t_total < budget_s:
+        t0 = time.perf_counter()
+        oracle.attn_decode(code, s.num_q_heads, s.num_kv_heads, s.head_dim, s.window,
+                           float(np.float32(s.scale)), float(np.float32(s.softcap)),
+                           int(s.k_eq_v), q, kc, vc, pb.block_table, pb.context_lens)
+        t_total += time.perf_counter() - t0
+        runs += 1
+    return dict(value=round(db.bytes * runs / t_total / 1e9, 4), unit="GB/s",
+                cores=oracle.num_threads(), kind="oracle",
+                sample=f"{runs} full passes of the oracle's decode attention over the same "
+                       f"{pb.batch}-sequence batch ({db.bytes / 1e9:.3f} GB of K/V each), "
+                       f"{t_total:.1f} s total")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--copies", type=int, default=4, help="cache copies rotated over steps")
+    ap.add_argument("--no-extra", action="store_true", help="headline decode workload only")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- headline: soft-capped decode -------------------------------------------------
+    head = DecodeBench("softcap_decode_bf16", args.copies, dev)
+    wall, w_ms, a_ms = time_steps(head.write, head.attend, args.steps, args.warmup)
+    value = head.bytes / (wall * 1e-3) / 1e9
+    achieved = head.bytes / (a_ms * 1e-3) / 1e9
+    log(f"softcap_decode: step {wall * 1e3:.1f} us (write {w_ms * 1e3:.1f} us, attention "
+        f"{a_ms * 1e3:.1f} us) -> {achieved:.0f} GB/s attention, {value:.0f} GB/s per step")
+    result = {
+        "metric": "decode attn KV GB/s (% HBM peak); prefill attn TFLOP/s (% MFMA peak)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "softcap_decode_bf16", "batch": head.pb.batch,
+                   "context_lens": "U[512,4096] seeded", "num_q_heads": 8, "num_kv_heads": 4,
+                   "head_dim": 256, "softcap": 50.0, "scale": 0.0625, "block_size": BS,
+                   "step": "kv_cache_write(32 new tokens) + attn_decode",
+                   "kv_bytes_per_step": head.bytes, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "attn_decode (split-K + combine)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "launch_us": round(a_ms * 1e3, 2), "bytes_per_launch": head.bytes},
+    }
+    if not args.no_extra:
+        extra = {}
+        for name in ("sliding_decode_bf16", "kv_shared_decode_bf16"):
+            db = DecodeBench(name, 2 if name == "kv_shared_decode_bf16" else args.copies, dev)
+            wall_x, w_x, a_x = time_steps(db.write, db.attend, max(args.steps // 2, 5),
+                                          max(args.warmup // 2, 2))
+            gbs = db.bytes / (a_x * 1e-3) / 1e9
+            log(f"{name}: attention {a_x * 1e3:.1f} us -> {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%})")
+            extra[name] = {"attn_us": round(a_x * 1e3, 2), "write_us": round(w_x * 1e3, 2),
+                           "kv_bytes": db.bytes, "attn_GBps": round(gbs, 1),
+                           "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                           "step_ms": round(wall_x, 4)}
+            del db
+            torch.cuda.empty_cache()
+        pf = PrefillBench(dev)
+        nl = len(pf.layers)
+        wall_p, w_p, a_p = time_steps(pf.write, pf.attend, max(args.steps // 5, 3),
+                                      max(args.warmup // 5, 1), inner=nl)
+        attn_ms = a_p * nl
+        tf = pf.flops / (attn_ms * 1e-3) / 1e12
+        log(f"chunked_prefill: 6-layer attention {attn_ms:.3f} ms -> {tf:.1f} TFLOP/s "
+            f"({tf / BF16_PEAK_TFLOPS:.1%}), step {wall_p:.3f} ms")
+        extra["chunked_prefill_bf16"] = {
+            "layers": nl, "attn_ms": round(attn_ms, 4), "write_ms": round(w_p * nl, 4),
+            "step_ms": round(wall_p, 4), "flops": pf.flops, "attn_TFLOPs": round(tf, 2),
+            "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
+            "per_layer_attn_ms": round(a_p, 4)}
+        result["extra"] = extra
+        del pf
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_decode(head, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,176 @@
+/*
+ * gemma_attn.h -- C ABI of the MI355X (gfx950) paged-KV Gemma-style attention library.
+ *
+ * Three operations make up one attention layer's hot path:
+ *   ga_kv_cache_write  RMSNorm of q/k/v, rotary embedding of q/k, scatter of k/v into pages;
+ *   ga_attn_decode     one query per sequence against its paged cache (split-K flash decoding);
+ *   ga_attn_prefill    a chunk of new queries per sequence against its paged cache (MFMA flash
+ *                      attention with the exact band + causal mask).
+ *
+ * Sources, cited by key:
+ *   [KUNLUN] "Gemma 4 模型架构解析" -- the Gemma 4 adaptation guide for vLLM-Kunlun: 挑战 1-3
+ *            (per-layer type, head size, k_eq_v), 挑战 5 (RoPE frequencies), §4 (shared KV),
+ *            §6.3 (slot formula), §6.4 (write path), §6.5 (paged read path).
+ *   [MNN]    "MNN 支持 Gemma4 全系列：PLE、KV共享与多模态": §2.2 (dual RoPE: head size 256 with
+ *            theta 1e4 on sliding layers, 512 with 1e6 on global ones), §6.1 (q/k/v norms,
+ *            attention scale 1.0), §6.2 (K=V and per-layer-type KV head counts).
+ *   [INFLM]  "Feat/add gemma3 model" (InfiniLM pull request 581): Gemma-2 §1 (logit soft cap
+ *            after scaling, before mask and softmax; scale from query_pre_attn_scalar),
+ *            Gemma-3 §3 (band + causal mask for prefill and chunked prefill, decode reads the
+ *            last min(len, W) keys, head-first GQA), and its hardening table (reject bad
+ *            configurations loudly, never return silently wrong results).
+ *
+ * Conventions for every call
+ *   - Pointers marked DEVICE are device (HBM) addresses; HOST ones are host addresses.  All
+ *     buffers are owned by the caller; the library allocates nothing, frees nothing and keeps
+ *     no state between calls, so it is safe to call from several host threads.
+ *   - `stream` is a hipStream_t (NULL: the default stream).  Every call only enqueues work on
+ *     it and returns; nothing is synchronised.
+ *   - Scalar arguments and the params struct are checked on the host before anything is
+ *     enqueued; a failing call returns an error and enqueues nothing.  Values that live in
+ *     device memory (lengths, block ids) cannot be read by the host without a copy: validate
+ *     them with ga_check_metadata_host on host copies.  The kernels clamp every page index and
+ *     block id into the buffers they were given, so bad metadata yields wrong numbers but no
+ *     out-of-bounds access.
+ *   - ga_last_error() returns a thread-local, human-readable reason for the last failure.
+ *
+ * Paged cache layout (block_size 16, the default page size of vLLM's paged cache; [KUNLUN] §6.3
+ * gives the slot arithmetic):
+ *   k_cache: [num_blocks][num_kv_heads][16][head_dim]   key rows, head_dim contiguous
+ *   v_cache: [num_blocks][num_kv_heads][head_dim][16]   value columns, the 16 keys contiguous
+ *   Token position t of sequence b lives in block block_table[b][t / 16], row t % 16.
+ *   The value page is stored transposed so that the matrix-core operand of P.V reads 16
+ *   contiguous bytes per lane; with k_eq_v there is no v_cache and values are read from k_cache.
+ */
+#ifndef GEMMA_ATTN_H
+#define GEMMA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GA_OK = 0,
+  GA_ERR_INVALID_ARG = 1, /* a pointer, size or parameter violates this header */
+  GA_ERR_UNSUPPORTED = 2, /* well-formed but not implemented (head_dim, group size, dtype) */
+  GA_ERR_WORKSPACE = 3,   /* decode workspace missing or smaller than ga_decode_workspace_bytes */
+  GA_ERR_HIP = 4          /* the HIP runtime reported an error when enqueuing a kernel */
+} ga_status;
+
+typedef enum {
+  GA_FP32 = 0, /* q, k, v, caches and out are float */
+  GA_BF16 = 1  /* ... are bfloat16 (round-to-nearest-even on every store) */
+} ga_dtype;
+
+/* Per-layer constants ([KUNLUN] 挑战 1-2: every layer picks head size, RoPE base and window
+ * from its type; [MNN] §2.2, §6.1-6.2). */
+typedef struct {
+  int32_t dtype;        /* ga_dtype */
+  int32_t num_q_heads;  /* Hq >= 1 */
+  int32_t num_kv_heads; /* Hkv >= 1, Hq % Hkv == 0; query head h reads kv head h / (Hq/Hkv) */
+  int32_t head_dim;     /* D: 128, 256 or 512 */
+  int32_t block_size;   /* tokens per page: must be 16 */
+  int32_t window;       /* W > 0: sliding layer, a query at position t sees keys t-W+1 .. t;
+                           W == 0: global layer (keys 0 .. t); W < 0: GA_ERR_INVALID_ARG */
+  float scale;          /* score = scale * q.k (1.0 for Gemma 4; 1/sqrt(query_pre_attn_scalar)
+                           for Gemma 2); must be finite */
+  float softcap;        /* > 0: score <- softcap * tanh(score / softcap) after scaling and
+                           before mask and softmax; 0: off; < 0 or non-finite: invalid */
+  int32_t k_eq_v;       /* 1: one cache (k_cache) serves as keys and values; v, v_cache and
+                           v_norm_w must then be NULL */
+  float rope_theta;     /* RoPE base (1e4 sliding, 1e6 global); 0: no rotation; < 0 invalid */
+  float rms_eps;        /* RMSNorm epsilon, >= 0 (Gemma layers use 1e-6) */
+} ga_layer_params;
+
+/* Norm + rotate + scatter the new tokens of a batch ([KUNLUN] §4.3 forward of a layer that
+ * owns its cache: k_norm, RoPE on q and k, v_norm; §6.3-6.4 slot and write path; [MNN] §6.1).
+ *   q            DEVICE [total_tokens][Hq][D]   raw query in; normalised and rotated query out
+ *                (in place).  May be NULL (only k/v are written).
+ *   k            DEVICE [total_tokens][Hkv][D]  raw keys.
+ *   v            DEVICE [total_tokens][Hkv][D]  raw values; NULL iff k_eq_v.
+ *   q_norm_w,
+ *   k_norm_w,
+ *   v_norm_w     DEVICE float [D] effective RMSNorm weights, or NULL for "no norm" on that
+ *                tensor.  y = x / sqrt(mean(x^2) + eps) * w.  v_norm_w must be NULL if k_eq_v.
+ *   cu_seqlens   DEVICE int32 [batch+1]: the new tokens of sequence b are rows
+ *                cu_seqlens[b] .. cu_seqlens[b+1]-1; cu_seqlens[batch] == total_tokens.
+ *   context_lens DEVICE int32 [batch]: tokens of sequence b after this write; its new tokens
+ *                take positions context_lens[b] - n_b .. context_lens[b] - 1.
+ *   block_table  DEVICE int32 [batch][max_blocks].
+ *   k_cache, v_cache  DEVICE, layouts above; v_cache NULL iff k_eq_v.  num_blocks = pages in each.
+ * Rotation: pair (k, k + D/2) turns by angle t * theta^(-2k/D), with the angle formed and the
+ * whole norm + rotation evaluated in double precision and rounded once into the storage type.
+ * Values are normalised but never rotated. */
+ga_status ga_kv_cache_write(const ga_layer_params* p, void* q, const void* k, const void* v,
+                            const float* q_norm_w, const float* k_norm_w, const float* v_norm_w,
+                            const int32_t* cu_seqlens, const int32_t* context_lens,
+                            const int32_t* block_table, int32_t max_blocks, int32_t batch,
+                            int32_t total_tokens, void* k_cache, void* v_cache,
+                            int64_t num_blocks, void* stream);
+
+/* Bytes of DEVICE scratch that ga_attn_decode needs for this shape (0 if none).  The value
+ * depends only on the arguments, never on device data. */
+size_t ga_decode_workspace_bytes(const ga_layer_params* p, int32_t batch,
+                                 int32_t max_context_len);
+
+/* Decode attention: one query per sequence, at position context_lens[b] - 1 ([INFLM] Gemma-3
+ * §3: a sliding layer reads only the last min(len, W) keys; [KUNLUN] §6.5 paged read).
+ *   q            DEVICE [batch][Hq][D], already normalised and rotated (ga_kv_cache_write).
+ *   k_cache, v_cache  DEVICE (v_cache NULL iff k_eq_v); num_blocks pages each.
+ *   block_table  DEVICE int32 [batch][max_blocks].
+ *   context_lens DEVICE int32 [batch], each in 1 .. max_context_len (the current token counts).
+ *   max_context_len  HOST bound on context_lens, used to size the launch; must satisfy
+ *                max_context_len <= max_blocks * 16.
+ *   out          DEVICE [batch][Hq][D] in the storage dtype.
+ *   workspace    DEVICE scratch of at least ga_decode_workspace_bytes(p, batch,
+ *                max_context_len) bytes, 256-byte aligned; contents need no initialisation
+ *                and are overwritten.  Concurrent calls must not share it. */
+ga_status ga_attn_decode(const ga_layer_params* p, const void* q, const void* k_cache,
+                         const void* v_cache, int64_t num_blocks, const int32_t* block_table,
+                         int32_t max_blocks, const int32_t* context_lens, int32_t batch,
+                         int32_t max_context_len, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Prefill / chunked prefill: the n_b new queries of each sequence, packed, against its cache
+ * (the chunk's own keys must already be written).  Query i of sequence b sits at position
+ * t = past_b + i with past_b = context_lens[b] - n_b and sees keys max(0, t-W+1) .. t (W = 0:
+ * 0 .. t) ([INFLM] Gemma-3 §3: exact band + causal mask, also for chunked prefill).
+ *   q            DEVICE [total_q][Hq][D], normalised and rotated.
+ *   cu_seqlens_q DEVICE int32 [batch+1], cu_seqlens_q[batch] == total_q.
+ *   context_lens DEVICE int32 [batch] = past_b + n_b.
+ *   max_q_len    HOST bound on every n_b (sizes the launch); max_q_len <= max_blocks * 16.
+ *   out          DEVICE [total_q][Hq][D]. */
+ga_status ga_attn_prefill(const ga_layer_params* p, const void* q,
+                          const int32_t* cu_seqlens_q, const void* k_cache,
+                          const void* v_cache, int64_t num_blocks,
+                          const int32_t* block_table, int32_t max_blocks,
+                          const int32_t* context_lens, int32_t batch, int32_t total_q,
+                          int32_t max_q_len, void* out, void* stream);
+
+/* Checks, on HOST copies, the metadata the kernels read from device memory:
+ *   cu_seqlens (HOST int32 [batch+1], may be NULL meaning one new token per sequence):
+ *     starts at 0, non-decreasing;
+ *   context_lens (HOST int32 [batch]): n_b <= context_lens[b] <= max_blocks * 16, and >= 1
+ *     when require_nonempty;
+ *   block_table (HOST int32 [batch][max_blocks]): every page a sequence uses holds a block id
+ *     in [0, num_blocks), and no two written slots of the call coincide.
+ * Returns GA_OK or GA_ERR_INVALID_ARG (reason in ga_last_error()). */
+ga_status ga_check_metadata_host(const ga_layer_params* p, const int32_t* cu_seqlens,
+                                 const int32_t* context_lens, const int32_t* block_table,
+                                 int32_t batch, int32_t max_blocks, int64_t num_blocks,
+                                 int32_t require_nonempty);
+
+/* Static name of a status code. */
+const char* ga_status_string(ga_status s);
+
+/* Thread-local reason of the most recent failing call on this thread ("" if none). */
+const char* ga_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMMA_ATTN_H */

@@ -42,6 +42,8 @@ def _load():
         lib = ctypes.CDLL(build())
         P = ctypes.c_void_p
         i32, i64, dbl = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        lib.ref_num_threads.restype = ctypes.c_int
+        lib.ref_num_threads.argtypes = []
         lib.ref_double_to_bf16.restype = ctypes.c_uint16
         lib.ref_double_to_bf16.argtypes = [dbl]
         lib.ref_bf16_to_double.restype = dbl
@@ -82,6 +84,11 @@ def _elem(dtype_code):
 
 
 # ------------------------------------------------------------------ scalar helpers --------
+
+def num_threads() -> int:
+    """Threads the oracle's parallel loops use (OpenMP)."""
+    return int(_load().ref_num_threads())
+
 
 def double_to_bf16(x: float) -> int:
     """Round one double to bf16 (nearest, ties to even); returns the 16-bit pattern."""

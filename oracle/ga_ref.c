@@ -46,12 +46,24 @@
  * dtype code: 0 = fp32 (float storage), 1 = bf16 (uint16_t storage, round-to-nearest-even).
  */
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 #define REF_FP32 0
 #define REF_BF16 1
+
+/* Threads the parallel loops below will use (1 without OpenMP). */
+int ref_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
 
 /* ---------------------------------------------------------------- number formats --- */
 

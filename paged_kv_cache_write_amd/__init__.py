@@ -1,0 +1,192 @@
+"""Python binding of libgemma_attn.so (paged KV write + Gemma-style attention on MI355X).
+
+Argument marshalling only: every step of the computation runs in the library's HIP kernels.
+torch tensors supply device memory and the current HIP stream.  The C ABI is documented in
+include/gemma_attn.h; each function here has the same name without the ``ga_`` prefix.
+
+If the shared library is missing this module raises on first use: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libgemma_attn.so")
+
+GA_FP32, GA_BF16 = 0, 1
+BLOCK_SIZE = 16
+STATUS = {0: "GA_OK", 1: "GA_ERR_INVALID_ARG", 2: "GA_ERR_UNSUPPORTED", 3: "GA_ERR_WORKSPACE",
+          4: "GA_ERR_HIP"}
+
+
+class GAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class LayerParams(ctypes.Structure):
+    """Mirror of ga_layer_params."""
+    _fields_ = [("dtype", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("softcap", ctypes.c_float),
+                ("k_eq_v", ctypes.c_int32), ("rope_theta", ctypes.c_float),
+                ("rms_eps", ctypes.c_float)]
+
+
+def layer_params(dtype, num_q_heads: int, num_kv_heads: int, head_dim: int, window: int = 0,
+                 scale: float = 1.0, softcap: float = 0.0, k_eq_v: bool = False,
+                 rope_theta: float = 10000.0, rms_eps: float = 1e-6,
+                 block_size: int = BLOCK_SIZE) -> LayerParams:
+    """dtype: torch.float32 / torch.bfloat16, or "fp32" / "bf16"."""
+    code = GA_BF16 if dtype in (torch.bfloat16, "bf16", GA_BF16) else GA_FP32
+    return LayerParams(code, num_q_heads, num_kv_heads, head_dim, block_size, window, scale,
+                       softcap, int(bool(k_eq_v)), rope_theta, rms_eps)
+
+
+_lib = None
+
+
+def load_library():
+    """Load the in-tree shared library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "(there is no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    PP = ctypes.POINTER(LayerParams)
+    lib.ga_kv_cache_write.restype = ctypes.c_int
+    lib.ga_kv_cache_write.argtypes = [PP, P, P, P, P, P, P, P, P, P, i32, i32, i32, P, P, i64, P]
+    lib.ga_decode_workspace_bytes.restype = sz
+    lib.ga_decode_workspace_bytes.argtypes = [PP, i32, i32]
+    lib.ga_attn_decode.restype = ctypes.c_int
+    lib.ga_attn_decode.argtypes = [PP, P, P, P, i64, P, i32, P, i32, i32, P, P, sz, P]
+    lib.ga_attn_prefill.restype = ctypes.c_int
+    lib.ga_attn_prefill.argtypes = [PP, P, P, P, P, i64, P, i32, P, i32, i32, i32, P, P]
+    lib.ga_check_metadata_host.restype = ctypes.c_int
+    lib.ga_check_metadata_host.argtypes = [PP, P, P, P, i32, i32, i64, i32]
+    lib.ga_status_string.restype = ctypes.c_char_p
+    lib.ga_status_string.argtypes = [ctypes.c_int]
+    lib.ga_last_error.restype = ctypes.c_char_p
+    lib.ga_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _raise_on(status: int):
+    if status != 0:
+        raise GAError(status, load_library().ga_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, device: bool = True):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _elem(p: LayerParams):
+    return torch.bfloat16 if p.dtype == GA_BF16 else torch.float32
+
+
+def kv_cache_write(p: LayerParams, q, k, v, q_norm_w, k_norm_w, v_norm_w, cu_seqlens,
+                   context_lens, block_table, k_cache, v_cache, stream=None) -> None:
+    """ga_kv_cache_write: norm + RoPE of q (in place) and k, norm of v, scatter into pages."""
+    lib = load_library()
+    et = _elem(p)
+    st = lib.ga_kv_cache_write(
+        ctypes.byref(p), _ptr(q, "q", et), _ptr(k, "k", et), _ptr(v, "v", et),
+        _ptr(q_norm_w, "q_norm_w", torch.float32), _ptr(k_norm_w, "k_norm_w", torch.float32),
+        _ptr(v_norm_w, "v_norm_w", torch.float32), _ptr(cu_seqlens, "cu_seqlens", torch.int32),
+        _ptr(context_lens, "context_lens", torch.int32),
+        _ptr(block_table, "block_table", torch.int32), block_table.shape[1],
+        context_lens.shape[0], k.shape[0], _ptr(k_cache, "k_cache", et),
+        _ptr(v_cache, "v_cache", et), k_cache.shape[0], _stream(stream))
+    _raise_on(st)
+
+
+def decode_workspace_bytes(p: LayerParams, batch: int, max_context_len: int) -> int:
+    return int(load_library().ga_decode_workspace_bytes(ctypes.byref(p), batch, max_context_len))
+
+
+def decode_workspace(p: LayerParams, batch: int, max_context_len: int, device="cuda"):
+    """A device byte buffer large enough for attn_decode on this shape."""
+    n = decode_workspace_bytes(p, batch, max_context_len)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def attn_decode(p: LayerParams, q, k_cache, v_cache, block_table, context_lens,
+                max_context_len: int, out=None, workspace=None, stream=None):
+    """ga_attn_decode: returns out [B, Hq, D]."""
+    lib = load_library()
+    et = _elem(p)
+    B = context_lens.shape[0]
+    if out is None:
+        out = torch.empty((B, p.num_q_heads, p.head_dim), dtype=et, device=q.device)
+    if workspace is None:
+        workspace = decode_workspace(p, B, max_context_len, q.device)
+    st = lib.ga_attn_decode(
+        ctypes.byref(p), _ptr(q, "q", et), _ptr(k_cache, "k_cache", et),
+        _ptr(v_cache, "v_cache", et), k_cache.shape[0],
+        _ptr(block_table, "block_table", torch.int32), block_table.shape[1],
+        _ptr(context_lens, "context_lens", torch.int32), B, int(max_context_len),
+        _ptr(out, "out", et), _ptr(workspace, "workspace"), workspace.numel(), _stream(stream))
+    _raise_on(st)
+    return out
+
+
+def attn_prefill(p: LayerParams, q, cu_seqlens_q, k_cache, v_cache, block_table, context_lens,
+                 max_q_len: int, out=None, stream=None):
+    """ga_attn_prefill: returns out [total_q, Hq, D]."""
+    lib = load_library()
+    et = _elem(p)
+    if out is None:
+        out = torch.empty_like(q)
+    st = lib.ga_attn_prefill(
+        ctypes.byref(p), _ptr(q, "q", et), _ptr(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+        _ptr(k_cache, "k_cache", et), _ptr(v_cache, "v_cache", et), k_cache.shape[0],
+        _ptr(block_table, "block_table", torch.int32), block_table.shape[1],
+        _ptr(context_lens, "context_lens", torch.int32), context_lens.shape[0], q.shape[0],
+        int(max_q_len), _ptr(out, "out", et), _stream(stream))
+    _raise_on(st)
+    return out
+
+
+def check_metadata_host(p: LayerParams, cu_seqlens, context_lens, block_table, num_blocks: int,
+                        require_nonempty: bool = True) -> None:
+    """ga_check_metadata_host on host (CPU) int32 tensors; raises GAError when invalid."""
+    lib = load_library()
+    cu = None if cu_seqlens is None else cu_seqlens.detach().cpu().to(torch.int32).contiguous()
+    cl = context_lens.detach().cpu().to(torch.int32).contiguous()
+    bt = block_table.detach().cpu().to(torch.int32).contiguous()
+    st = lib.ga_check_metadata_host(
+        ctypes.byref(p), None if cu is None else ctypes.c_void_p(cu.data_ptr()),
+        ctypes.c_void_p(cl.data_ptr()), ctypes.c_void_p(bt.data_ptr()), cl.shape[0],
+        bt.shape[1], int(num_blocks), int(bool(require_nonempty)))
+    _raise_on(st)
+
+
+__all__ = ["LayerParams", "layer_params", "kv_cache_write", "attn_decode", "attn_prefill",
+           "decode_workspace_bytes", "decode_workspace", "check_metadata_host", "GAError",
+           "load_library", "LIB_PATH", "GA_FP32", "GA_BF16", "BLOCK_SIZE"]

@@ -1,0 +1,104 @@
+// device_common.hpp -- small device helpers shared by the gfx950 kernels of this library.
+//
+// Everything here is CDNA4-specific: 64-lane wavefronts, the bf16 matrix-core instructions
+// v_mfma_f32_16x16x32_bf16 / v_mfma_f32_16x16x16_bf16 and their register layouts.
+//
+// MFMA register layouts used throughout (l = lane 0..63, j = l / 16, c = l % 16):
+//   16x16x32 bf16:  A[i][k]: lane l holds row i = c, k = 8j .. 8j+7   (8 bf16)
+//                   B[k][n]: lane l holds col n = c, k = 8j .. 8j+7   (8 bf16)
+//   16x16x16 bf16:  A[i][k]: row i = c, k = 4j .. 4j+3                (4 bf16)
+//                   B[k][n]: col n = c, k = 4j .. 4j+3                (4 bf16)
+//   output D[i][n] (both): lane l holds D[4j + r][c] in register r = 0..3.
+// The contraction index k is only ever used to pair A with B, so any assignment of k-slots
+// to actual elements is correct as long as A and B use the same one.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ga {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+typedef __attribute__((ext_vector_type(4))) short short4_t;
+typedef __attribute__((ext_vector_type(4))) float float4_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+constexpr int kWave = 64;
+constexpr int kPage = 16;  // tokens per page (block_size)
+
+// ------------------------------------------------------------------------ bf16 <-> fp32 ---
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Two fp32 -> packed bf16x2 (lo in bits 0..15), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// double -> bf16 with a single rounding (nearest, ties to even): round to fp32 toward zero,
+// make the result sticky (round-to-odd) if anything was dropped, then round to bf16.  fp32
+// keeps 16 more bits than bf16, so the second rounding sees the exact tie/no-tie information.
+__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
+  if (x != x) return (uint16_t)0x7fc0u;
+  float fz = __double2float_rz(x);
+  uint32_t u = __float_as_uint(fz);
+  if ((double)fz != x && (u & 0x7f800000u) != 0x7f800000u) u |= 1u;
+  return f32_to_bf16(__uint_as_float(u));
+}
+
+// ------------------------------------------------------------------------ MFMA --------------
+
+__device__ __forceinline__ float4_t mfma_16x16x32(const bf16x8_t& a, const bf16x8_t& b,
+                                                  const float4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float4_t mfma_16x16x16(const short4_t& a, const short4_t& b,
+                                                  const float4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+__device__ __forceinline__ short4_t as_short4(const u32x2_t& v) {
+  return __builtin_bit_cast(short4_t, v);
+}
+
+// ------------------------------------------------------------------------ cross-lane -------
+
+__device__ __forceinline__ float xor_max(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, kWave));
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// Soft cap on the log2 scale: returns cap_log2 * tanh(s * inv_cap), tanh from exp2 with
+// saturation (exp2 overflow -> +inf -> tanh = 1).  cap_log2 = cap * log2(e), inv_cap = scale/cap.
+__device__ __forceinline__ float softcap_log2(float s, float inv_cap, float cap_log2) {
+  const float x = s * inv_cap;
+  const float e = __builtin_amdgcn_exp2f(fabsf(x) * 2.8853900817779268f);  // exp(2|x|)
+  const float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+  return cap_log2 * copysignf(t, x);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace ga

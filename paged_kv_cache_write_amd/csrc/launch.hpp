@@ -1,0 +1,63 @@
+// launch.hpp -- internal interface between the C ABI (api.cpp) and the kernel files.
+// The host side validates everything before it fills one of these structs; the launchers
+// only enqueue kernels and report the HIP status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ga {
+
+struct KvWriteLaunch {
+  bool dtype_bf16;
+  int D, Hq, Hkv, k_eq_v;
+  float rope_theta, rms_eps;
+  void* q;
+  const void* k;
+  const void* v;
+  const float *wq, *wk, *wv;
+  const int32_t* cu_seqlens;
+  const int32_t* context_lens;
+  const int32_t* block_table;
+  int32_t max_blocks, batch, total_tokens;
+  void* k_cache;
+  void* v_cache;
+  int64_t num_blocks;
+};
+
+// Shared description of an attention call (decode or prefill).
+struct AttnLaunch {
+  bool dtype_bf16;
+  int D, Hq, Hkv, window, k_eq_v;
+  float scale, softcap;
+  const void* q;
+  const int32_t* cu_seqlens_q;  // prefill only
+  const void* k_cache;
+  const void* v_cache;
+  int64_t num_blocks;
+  const int32_t* block_table;
+  int32_t max_blocks;
+  const int32_t* context_lens;
+  int32_t batch;
+  int32_t max_context_len;  // decode: host bound on context_lens
+  int32_t total_q, max_q_len;  // prefill
+  void* out;
+  void* workspace;
+};
+
+// Split-K plan of a decode call; a pure function of the host arguments.
+struct DecodePlan {
+  int pages_per_split;  // multiple of 8
+  int num_splits;       // splits of the longest visible key range
+  size_t workspace_bytes;
+};
+
+DecodePlan plan_decode(int D, int Hq, int Hkv, int window, int batch, int max_context_len,
+                       bool bf16);
+
+hipError_t launch_kv_write(const KvWriteLaunch& a, hipStream_t s);
+hipError_t launch_decode(const AttnLaunch& a, const DecodePlan& plan, hipStream_t s);
+hipError_t launch_prefill(const AttnLaunch& a, hipStream_t s);
+
+}  // namespace ga

@@ -1,0 +1,174 @@
+"""Shared set-up for the GPU parity tests: seeded inputs on the device, the library's calls,
+and comparisons against the CPU oracle.
+
+The oracle always reads the bytes the GPU stored (normalised q, cache pages) for the
+attention-stage checks, so the attention tolerance measures the attention kernels alone; the
+write stage is compared separately, element by element, against the oracle's own write.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import paged_kv_cache_write_amd as ga
+import workloads as wl
+
+BF16_MAX_ABS, BF16_MEAN_ABS = 2e-2, 2e-3   # bf16 inputs, fp32 accumulation
+FP32_MAX_ABS = 1e-4
+
+
+def dtype_code(spec):
+    return oracle.BF16 if spec.dtype == "bf16" else oracle.FP32
+
+
+def params(spec) -> ga.LayerParams:
+    return ga.layer_params(spec.dtype, spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
+                           window=spec.window, scale=spec.scale, softcap=spec.softcap,
+                           k_eq_v=spec.k_eq_v, rope_theta=spec.rope_theta, rms_eps=spec.rms_eps)
+
+
+def i32(a, device):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+
+class PagedCase:
+    """Device caches + block table of one layer, filled through ga.kv_cache_write."""
+
+    def __init__(self, spec: wl.LayerSpec, pb: wl.PagedBatch, seed: int, device="cuda"):
+        self.spec, self.pb, self.seed, self.dev = spec, pb, seed, torch.device(device)
+        self.p = params(spec)
+        self.kc, self.vc = wl.empty_caches(spec, pb.num_blocks, self.dev)
+        w = wl.norm_weights(spec, seed)
+        self.w_cpu = w
+        self.w = [None if x is None else x.to(self.dev) for x in w]
+        self.bt = i32(pb.block_table, self.dev)
+
+    # -- writes -------------------------------------------------------------------------
+    def write(self, context_lens, n_new, seed, q_scale=1.0, with_q=True, device_gen=False):
+        """Write n_new[b] fresh tokens ending at context_lens[b]; returns (raw q, k, v, q after
+        the call on the device, cu_seqlens, context_lens).  Raw inputs are drawn on the CPU
+        (device_gen=False, so the oracle can replay them) or on the GPU (large fills)."""
+        cl = np.asarray(context_lens, np.int32)
+        nn = np.asarray(n_new, np.int32)
+        cu = np.concatenate([[0], np.cumsum(nn)]).astype(np.int32)
+        T = int(cu[-1])
+        q, k, v = wl.raw_qkv(self.spec, T, seed, q_scale=q_scale,
+                             device=self.dev if device_gen else "cpu")
+        qd = q.to(self.dev) if with_q else None
+        ga.check_metadata_host(self.p, torch.from_numpy(cu), torch.from_numpy(cl),
+                               torch.from_numpy(self.pb.block_table), self.pb.num_blocks,
+                               require_nonempty=False)
+        ga.kv_cache_write(self.p, qd, k.to(self.dev), None if v is None else v.to(self.dev),
+                          *self.w, i32(cu, self.dev), i32(cl, self.dev), self.bt, self.kc,
+                          self.vc)
+        return q, k, v, qd, cu, cl
+
+    def write_all(self, lens, seed):
+        """Write every position 0 .. lens[b]-1 in one call (no query)."""
+        return self.write(lens, lens, seed, with_q=False)
+
+    def host_caches(self):
+        nb = wl.to_numpy_bits
+        return nb(self.kc), (None if self.vc is None else nb(self.vc))
+
+    def oracle_write(self, kc, vc, q, k, v, cu, cl):
+        """Apply the oracle's write to host caches (in place); returns the oracle's q̂."""
+        return oracle_write(self.spec, self.w_cpu, self.pb.block_table, kc, vc, q, k, v, cu, cl)
+
+    # -- attention ------------------------------------------------------------------------
+    def prefill(self, q_dev, cu, cl, max_q_len=None):
+        return ga.attn_prefill(self.p, q_dev, i32(cu, self.dev), self.kc, self.vc, self.bt,
+                               i32(cl, self.dev), int(np.diff(cu).max()) if max_q_len is None
+                               else max_q_len)
+
+    def decode(self, q_dev, cl, max_context_len=None):
+        return ga.attn_decode(self.p, q_dev, self.kc, self.vc, self.bt, i32(cl, self.dev),
+                              int(np.max(cl)) if max_context_len is None else max_context_len)
+
+    def oracle_attention(self, q_dev, cu, cl, rows=None, caches=None):
+        s = self.spec
+        kc, vc = caches if caches is not None else self.host_caches()
+        return oracle.attention(dtype_code(s), s.num_q_heads, s.num_kv_heads, s.head_dim,
+                                s.window, float(np.float32(s.scale)), float(np.float32(s.softcap)),
+                                int(s.k_eq_v), wl.to_numpy_bits(q_dev), cu, kc, vc,
+                                self.pb.block_table, cl, rows=rows)
+
+
+def oracle_write(spec, w_cpu, block_table, kc, vc, q, k, v, cu, cl):
+    """The oracle's write of raw CPU tensors q (or None), k, v into host caches kc / vc
+    (numpy, in place); returns the oracle's normalised and rotated q (numpy) or None."""
+    nb = wl.to_numpy_bits
+    qh = None if q is None else nb(q)
+    wq, wk, wv = (None if x is None else x.numpy() for x in w_cpu)
+    oracle.kv_cache_write(dtype_code(spec), spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
+                          float(np.float32(spec.rope_theta)), float(np.float32(spec.rms_eps)),
+                          int(spec.k_eq_v), qh, nb(k), None if v is None else nb(v), wq, wk, wv,
+                          cu, cl, block_table, kc, vc)
+    return qh
+
+
+def assert_attn_close(got: torch.Tensor, ref: np.ndarray, dtype: str, rows=None, what=""):
+    g = got.float().cpu().numpy().astype(np.float64)
+    if rows is not None:
+        g, ref = g[rows], ref[rows]
+    assert np.isfinite(g).all(), f"{what}: non-finite GPU output"
+    err = np.abs(g - ref)
+    mx, mean = float(err.max()), float(err.mean())
+    if dtype == "bf16":
+        assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, f"{what}: max {mx:.3e} mean {mean:.3e}"
+    else:
+        assert mx <= FP32_MAX_ABS, f"{what}: max {mx:.3e}"
+    return mx, mean
+
+
+def assert_within_bf16_ulps(a: torch.Tensor, b: torch.Tensor, ulps: int = 2):
+    """Two bf16 results of the same math that differ only in summation order: each element
+    within `ulps` units in the last place of the larger magnitude (bf16 keeps 8 bits)."""
+    x, y = a.float().cpu(), b.float().cpu()
+    tol = ulps * torch.maximum(x.abs(), y.abs()) * 2.0 ** -7 + 1e-6
+    bad = (x - y).abs() > tol
+    assert not bad.any(), f"{int(bad.sum())} elements differ by more than {ulps} ulps"
+
+
+def ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Distance in units in the last place between two arrays of bf16 (uint16) or fp32 bits;
+    NaN == NaN counts as 0."""
+    if a.dtype == np.uint16:
+        ai, bi = a.astype(np.int64), b.astype(np.int64)
+        sign = 0x8000
+        nan_a = (ai & 0x7FFF) > 0x7F80
+        nan_b = (bi & 0x7FFF) > 0x7F80
+    else:
+        ai = a.view(np.uint32).astype(np.int64)
+        bi = b.view(np.uint32).astype(np.int64)
+        sign = 0x80000000
+        nan_a, nan_b = np.isnan(a), np.isnan(b)
+    # map sign-magnitude to a monotone integer line
+    ai = np.where(ai & sign, -(ai & (sign - 1)), ai)
+    bi = np.where(bi & sign, -(bi & (sign - 1)), bi)
+    d = np.abs(ai - bi)
+    d = np.where(nan_a & nan_b, 0, d)
+    d = np.where(nan_a ^ nan_b, np.iinfo(np.int64).max, d)
+    return d
+
+
+def compact_pages(case: PagedCase, seqs, lens):
+    """Copy only the pages that sequences `seqs` use into compact host caches, with a block
+    table renumbered to match (page gather by block id; no arithmetic on values)."""
+    bt = case.pb.block_table
+    ids, rows = [], []
+    for b in seqs:
+        npg = -(-int(lens[b]) // wl.BLOCK_SIZE)
+        start = len(ids)
+        ids.extend(int(x) for x in bt[b, :npg])
+        rows.append(np.arange(start, start + npg))
+    idx = torch.tensor(ids, dtype=torch.long, device=case.dev)
+    kc = wl.to_numpy_bits(case.kc.index_select(0, idx))
+    vc = None if case.vc is None else wl.to_numpy_bits(case.vc.index_select(0, idx))
+    width = max(len(r) for r in rows)
+    nbt = np.zeros((len(seqs), width), np.int32)
+    for i, r in enumerate(rows):
+        nbt[i, :len(r)] = r
+        nbt[i, len(r):] = r[-1] if len(r) else 0
+    return kc, vc, nbt

@@ -1,0 +1,188 @@
+"""GPU parity of ga_attn_decode / ga_attn_prefill against the oracle, on small ragged inputs
+that span several page pairs and ragged tails, plus exact mask probes."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_write_amd as ga
+import workloads as wl
+from harness import PagedCase, assert_attn_close, assert_within_bf16_ulps, i32
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode_case(spec, lens, seed, q_scale=1.0):
+    pb = wl.paged_batch(lens, np.ones(len(lens), np.int32), seed=seed)
+    case = PagedCase(spec, pb, seed)
+    past = [L - 1 for L in lens]
+    if max(past) > 0:
+        case.write(past, past, seed + 100, with_q=False)
+    q, k, v, qd, cu, cl = case.write(lens, [1] * len(lens), seed, q_scale=q_scale)
+    out = case.decode(qd, cl)
+    torch.cuda.synchronize()
+    ref = case.oracle_attention(qd, cu, cl)
+    return out, ref
+
+
+DECODE_CASES = [
+    # dtype, Hq, Hkv, D, W, cap, k_eq_v, lens
+    ("bf16", 8, 4, 256, 0, 50.0, False, [1, 2, 17, 31, 32, 33, 200, 513]),
+    ("bf16", 32, 16, 256, 64, 0.0, False, [1, 63, 64, 65, 100, 300]),
+    ("bf16", 32, 4, 512, 0, 0.0, True, [1, 16, 47, 700]),
+    ("bf16", 16, 1, 512, 100, 30.0, True, [5, 99, 100, 101, 450]),
+    ("bf16", 4, 4, 128, 17, 0.0, False, [1, 16, 17, 18, 333]),
+    ("bf16", 16, 1, 256, 0, 0.0, False, [129, 1000]),
+    ("fp32", 4, 2, 256, 128, 0.0, False, [1, 128, 129, 272]),
+    ("fp32", 8, 2, 512, 0, 20.0, True, [3, 150]),
+]
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D,W,cap,keqv,lens", DECODE_CASES)
+def test_decode_matches_oracle(dtype, Hq, Hkv, D, W, cap, keqv, lens):
+    spec = wl.LayerSpec(dtype, Hq, Hkv, D, window=W, softcap=cap, k_eq_v=keqv,
+                        scale=1.0 if cap == 0 else 1.0 / 16, rope_theta=1e4 if D < 512 else 1e6)
+    out, ref = _decode_case(spec, lens, seed=21)
+    assert_attn_close(out, ref, dtype, what=f"decode {dtype} D{D} G{Hq // Hkv} W{W} cap{cap}")
+
+
+def test_decode_softcap_binds():
+    """q scaled by 20 so that the cap of 50 dominates the scores."""
+    spec = wl.LayerSpec("bf16", 8, 4, 256, softcap=50.0, scale=1 / 16, norm_q=False,
+                        norm_k=False, norm_v=False)
+    out, ref = _decode_case(spec, [700, 1500, 33], seed=22, q_scale=20.0)
+    assert_attn_close(out, ref, "bf16", what="decode cap binds")
+
+
+PREFILL_CASES = [
+    # dtype, Hq, Hkv, D, W, cap, k_eq_v, (lens, news)
+    ("bf16", 8, 4, 256, 0, 0.0, False, ([70, 33, 200], [70, 33, 64])),
+    ("bf16", 32, 16, 256, 40, 0.0, False, ([300, 129], [77, 129])),
+    ("bf16", 32, 4, 512, 0, 0.0, False, ([260, 90], [100, 90])),
+    ("bf16", 32, 4, 512, 0, 0.0, True, ([260, 90], [100, 1])),
+    ("bf16", 8, 1, 512, 33, 25.0, True, ([140], [140])),
+    ("bf16", 4, 2, 128, 16, 10.0, False, ([1, 16, 17, 48], [1, 16, 17, 20])),
+    ("fp32", 4, 2, 256, 128, 0.0, False, ([256], [256])),
+    ("fp32", 8, 2, 512, 0, 0.0, True, ([90, 31], [30, 31])),
+]
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D,W,cap,keqv,ln", PREFILL_CASES)
+def test_prefill_matches_oracle(dtype, Hq, Hkv, D, W, cap, keqv, ln):
+    lens, news = ln
+    spec = wl.LayerSpec(dtype, Hq, Hkv, D, window=W, softcap=cap, k_eq_v=keqv,
+                        rope_theta=1e4 if D < 512 else 1e6)
+    pb = wl.paged_batch(lens, news, seed=31)
+    case = PagedCase(spec, pb, 31)
+    past = [L - n for L, n in zip(lens, news)]
+    if max(past) > 0:
+        case.write(past, past, 131, with_q=False)
+    q, k, v, qd, cu, cl = case.write(lens, news, 31)
+    out = case.prefill(qd, cu, cl)
+    torch.cuda.synchronize()
+    ref = case.oracle_attention(qd, cu, cl)
+    assert_attn_close(out, ref, dtype, what=f"prefill {dtype} D{D} W{W}")
+
+
+@pytest.mark.parametrize("past,n,W,keqv", [(5, 37, 4, False), (0, 40, 16, False),
+                                           (20, 33, 1, True), (31, 20, 0, False),
+                                           (48, 17, 17, True)])
+def test_one_hot_probes_are_bit_exact(past, n, W, keqv):
+    """Plant one key that beats every other score by ~200 (2^-288 underflows to 0 in fp32):
+    a query that sees it returns its value bit-exactly; one that does not never returns it.
+    Probes sit at window edges, page edges and the causal edge."""
+    D, L = 256, past + n
+    spec = wl.LayerSpec("bf16", 2, 1, D, window=W, rope_theta=0.0, k_eq_v=keqv,
+                        norm_q=False, norm_k=False, norm_v=False)
+    pb = wl.paged_batch([L], [n], seed=41)
+    dev = torch.device("cuda")
+    probes = {0, 15, 16, 17, past, L - W, L - W - 1, L - 1, past + W, past + W - 1}
+    for jstar in sorted(j for j in probes if 0 <= j < L):
+        case = PagedCase(spec, pb, 41)
+        k = torch.zeros(L, 1, D)
+        k[jstar, 0, 0] = 200.0
+        v = torch.zeros(L, 1, D) if not keqv else None
+        if v is not None:
+            v[:, 0, 1] = torch.arange(L, dtype=torch.float32) / 64.0
+            v[jstar, 0, 1] = -3.0
+        else:
+            k[:, 0, 1] = torch.arange(L, dtype=torch.float32) / 64.0
+            k[jstar, 0, 1] = -3.0
+        q = torch.zeros(n, 2, D)
+        q[:, :, 0] = 1.0
+        cu = np.array([0, L], np.int32)
+        bt = case.bt
+        kb = k.to(torch.bfloat16).to(dev)
+        vb = None if v is None else v.to(torch.bfloat16).to(dev)
+        ga.kv_cache_write(case.p, None, kb, vb, None, None, None, i32(cu, dev),
+                          i32([L], dev), bt, case.kc, case.vc)
+        qd = q.to(torch.bfloat16).to(dev)
+        cuq = np.array([0, n], np.int32)
+        out = case.prefill(qd, cuq, np.array([L], np.int32)).float().cpu()
+        for i in range(n):
+            t = past + i
+            vis = jstar <= t and (W == 0 or t - jstar < W)
+            got = out[i, :, 1]
+            if vis:
+                assert (got == -3.0).all(), (jstar, i)
+            else:
+                assert (got != -3.0).all(), (jstar, i)
+        # decode at the last position agrees bit-for-bit with the last prefill row
+        dec = case.decode(qd[-1:].contiguous(), np.array([L], np.int32)).float().cpu()
+        vis = jstar <= L - 1 and (W == 0 or L - 1 - jstar < W)
+        assert ((dec[0, :, 1] == -3.0).all()) == vis
+
+
+def test_sliding_decode_ignores_pages_before_the_window():
+    """NaN-poison every page that lies entirely before the window: output unchanged."""
+    spec = wl.LayerSpec("bf16", 8, 4, 256, window=100, rope_theta=1e4)
+    lens = [1000, 640, 101]
+    pb = wl.paged_batch(lens, [1, 1, 1], seed=51)
+    case = PagedCase(spec, pb, 51)
+    case.write([L - 1 for L in lens], [L - 1 for L in lens], 151, with_q=False)
+    q, k, v, qd, cu, cl = case.write(lens, [1, 1, 1], 51)
+    out1 = case.decode(qd, cl).clone()
+    for b, L in enumerate(lens):
+        first_page = (L - 100) // 16
+        for pg in range(first_page):
+            case.kc[int(pb.block_table[b, pg])] = float("nan")
+            case.vc[int(pb.block_table[b, pg])] = float("nan")
+    out2 = case.decode(qd, cl)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+
+
+def test_decode_equals_last_prefill_row_and_gqa_equals_repeated_heads():
+    spec = wl.LayerSpec("bf16", 8, 2, 256, window=50, rope_theta=1e4)
+    lens = [130, 77]
+    pb = wl.paged_batch(lens, lens, seed=61)
+    case = PagedCase(spec, pb, 61)
+    q, k, v, qd, cu, cl = case.write(lens, lens, 61)
+    pre = case.prefill(qd, cu, cl)
+    last = torch.from_numpy(cu[1:] - 1).long().cuda()
+    dec = case.decode(qd[last].contiguous(), cl)
+    torch.cuda.synchronize()
+    assert_within_bf16_ulps(dec, pre[last])
+    # GQA: the same layer with each kv head repeated 4x (MHA) gives the same output
+    spec2 = wl.LayerSpec("bf16", 8, 8, 256, window=50, rope_theta=1e4)
+    case2 = PagedCase(spec2, pb, 61)
+    case2.kc.copy_(case.kc.repeat_interleave(4, dim=1))
+    case2.vc.copy_(case.vc.repeat_interleave(4, dim=1))
+    pre2 = case2.prefill(qd, cu, cl)
+    torch.cuda.synchronize()
+    assert_within_bf16_ulps(pre2, pre)
+
+
+def test_k_eq_v_equals_separate_caches_holding_the_same_tensor():
+    spec = wl.LayerSpec("bf16", 16, 2, 512, window=0, k_eq_v=True, rope_theta=1e6)
+    lens = [300, 45]
+    pb = wl.paged_batch(lens, lens, seed=71)
+    case = PagedCase(spec, pb, 71)
+    q, k, v, qd, cu, cl = case.write(lens, lens, 71)
+    a = case.prefill(qd, cu, cl)
+    spec2 = wl.LayerSpec("bf16", 16, 2, 512, window=0, k_eq_v=False, rope_theta=1e6)
+    case2 = PagedCase(spec2, pb, 71)
+    case2.kc.copy_(case.kc)
+    case2.vc.copy_(case.kc.transpose(2, 3))
+    b = case2.prefill(qd, cu, cl)
+    torch.cuda.synchronize()
+    assert_within_bf16_ulps(a, b)
