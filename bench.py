@@ -7,9 +7,11 @@ measures the bf16 soft-capped decode workload (32 sequences, lengths U[512, 4096
 prefill workload (4 x 2048 new tokens after 6144 cached, 5 sliding + 1 global layer) and the
 two other decode workloads, each with its own roofline fraction.
 
-value = algorithmic KV bytes read by decode attention per step / wall time per step (GB/s).
-Inputs are resident in HBM; the caches are rotated over several copies so that the 256 MB
-last-level cache cannot hold a step's working set.
+value = algorithmic KV bytes read by decode attention per step / wall time per step (GB/s),
+with each step replayed from a HIP graph (as a serving loop would run it).  Inputs are
+resident in HBM; the caches are rotated over several copies so that the 256 MB last-level
+cache cannot hold a step's working set.  The roofline figure times the attention call alone:
+back-to-back calls between two HIP events on the launch stream.
 """
 from __future__ import annotations
 
@@ -182,31 +184,47 @@ class PrefillBench:
 
 # ----------------------------------------------------------------------------- timing ---------
 
-def time_steps(write, attend, steps, warmup, inner=1):
-    """Warm up, then time `steps` steps; every step is `inner` x (write, attend).  Returns
-    (wall ms per step, mean event ms of the writes, mean event ms of the attention calls)."""
+def capture_steps(step_fns):
+    """One HIP graph per step function (each runs the whole step: write + attention).  The
+    step is run eagerly first (warm-up, and the library's one-time device queries)."""
+    for f in step_fns:
+        f()
+    torch.cuda.synchronize()
+    graphs = []
+    for f in step_fns:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            f()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def time_graph_steps(graphs, steps, warmup):
+    """Wall-clock ms per step over `steps` graph replays (rotating over the graphs)."""
     for i in range(warmup):
-        for j in range(inner):
-            write(j)
-            attend(j)
+        graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps * inner)]
     t0 = time.perf_counter()
-    n = 0
     for i in range(steps):
-        for j in range(inner):
-            e = ev[n]
-            e[0].record()
-            write(i * inner + j if inner == 1 else j)
-            e[1].record()
-            attend(i * inner + j if inner == 1 else j)
-            e[2].record()
-            n += 1
+        graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3 / steps
-    w = np.mean([e[0].elapsed_time(e[1]) for e in ev])
-    a = np.mean([e[1].elapsed_time(e[2]) for e in ev])
-    return wall, float(w), float(a)
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def time_calls(fn, n, reps, warmup):
+    """Mean device ms of one call: `reps` calls fn(i) back to back on the current stream,
+    bracketed by two HIP events (the calls rotate over n inputs)."""
+    for i in range(warmup):
+        fn(i % n)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        fn(i % n)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
 
 
 def cpu_baseline_decode(db: DecodeBench, budget_s: float):
@@ -251,11 +269,16 @@ def main():
 
     # ---- headline: soft-capped decode -------------------------------------------------
     head = DecodeBench("softcap_decode_bf16", args.copies, dev)
-    wall, w_ms, a_ms = time_steps(head.write, head.attend, args.steps, args.warmup)
+    nc = len(head.kcs)
+    graphs = capture_steps([lambda c=c: (head.write(c), head.attend(c)) for c in range(nc)])
+    wall = time_graph_steps(graphs, args.steps, args.warmup)
+    a_ms = time_calls(head.attend, nc, args.steps, args.warmup)
+    w_ms = time_calls(head.write, nc, args.steps, args.warmup)
     value = head.bytes / (wall * 1e-3) / 1e9
     achieved = head.bytes / (a_ms * 1e-3) / 1e9
-    log(f"softcap_decode: step {wall * 1e3:.1f} us (write {w_ms * 1e3:.1f} us, attention "
-        f"{a_ms * 1e3:.1f} us) -> {achieved:.0f} GB/s attention, {value:.0f} GB/s per step")
+    log(f"softcap_decode: step {wall * 1e3:.1f} us (graph replay); attention call "
+        f"{a_ms * 1e3:.1f} us -> {achieved:.0f} GB/s; write call {w_ms * 1e3:.1f} us; "
+        f"{value:.0f} GB/s per step")
     result = {
         "metric": "decode attn KV GB/s (% HBM peak); prefill attn TFLOP/s (% MFMA peak)",
         "value": round(value, 2),
@@ -272,42 +295,57 @@ def main():
         "config": {"workload": "softcap_decode_bf16", "batch": head.pb.batch,
                    "context_lens": "U[512,4096] seeded", "num_q_heads": 8, "num_kv_heads": 4,
                    "head_dim": 256, "softcap": 50.0, "scale": 0.0625, "block_size": BS,
-                   "step": "kv_cache_write(32 new tokens) + attn_decode",
-                   "kv_bytes_per_step": head.bytes, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "attn_decode (split-K + combine)",
+                   "step": "kv_cache_write(32 new tokens) + attn_decode, replayed as a HIP graph",
+                   "kv_bytes_per_step": head.bytes, "cache_copies_rotated": nc,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "attn_decode (decode_stream_kernel + "
+                     "decode_merge_kernel)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "launch_us": round(a_ms * 1e3, 2), "bytes_per_launch": head.bytes},
+                     "call_us": round(a_ms * 1e3, 2), "bytes_per_call": head.bytes,
+                     "write_call_us": round(w_ms * 1e3, 2)},
     }
+    del graphs
     if not args.no_extra:
         extra = {}
         for name in ("sliding_decode_bf16", "kv_shared_decode_bf16"):
             db = DecodeBench(name, 2 if name == "kv_shared_decode_bf16" else args.copies, dev)
-            wall_x, w_x, a_x = time_steps(db.write, db.attend, max(args.steps // 2, 5),
-                                          max(args.warmup // 2, 2))
+            n = len(db.kcs)
+            gx = capture_steps([lambda c=c: (db.write(c), db.attend(c)) for c in range(n)])
+            wall_x = time_graph_steps(gx, max(args.steps // 2, 5), max(args.warmup // 2, 2))
+            a_x = time_calls(db.attend, n, max(args.steps // 2, 5), max(args.warmup // 2, 2))
             gbs = db.bytes / (a_x * 1e-3) / 1e9
-            log(f"{name}: attention {a_x * 1e3:.1f} us -> {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%})")
-            extra[name] = {"attn_us": round(a_x * 1e3, 2), "write_us": round(w_x * 1e3, 2),
-                           "kv_bytes": db.bytes, "attn_GBps": round(gbs, 1),
-                           "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
-                           "step_ms": round(wall_x, 4)}
-            del db
+            log(f"{name}: attention call {a_x * 1e3:.1f} us -> {gbs:.0f} GB/s "
+                f"({gbs / HBM_PEAK_GBS:.1%}); step {wall_x * 1e3:.1f} us")
+            extra[name] = {"attn_call_us": round(a_x * 1e3, 2), "kv_bytes": db.bytes,
+                           "attn_GBps": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                           "step_us": round(wall_x * 1e3, 2),
+                           "step_GBps": round(db.bytes / (wall_x * 1e-3) / 1e9, 1)}
+            del gx, db
             torch.cuda.empty_cache()
         pf = PrefillBench(dev)
         nl = len(pf.layers)
-        wall_p, w_p, a_p = time_steps(pf.write, pf.attend, max(args.steps // 5, 3),
-                                      max(args.warmup // 5, 1), inner=nl)
-        attn_ms = a_p * nl
+
+        def stack():
+            for li in range(nl):
+                pf.write(li)
+                pf.attend(li)
+        gp = capture_steps([stack])
+        wall_p = time_graph_steps(gp, max(args.steps // 5, 3), max(args.warmup // 5, 1))
+        a_layers = [time_calls(lambda i, li=li: pf.attend(li), 1, 3, 1) for li in range(nl)]
+        w_layers = [time_calls(lambda i, li=li: pf.write(li), 1, 3, 1) for li in range(nl)]
+        attn_ms = float(sum(a_layers))
         tf = pf.flops / (attn_ms * 1e-3) / 1e12
         log(f"chunked_prefill: 6-layer attention {attn_ms:.3f} ms -> {tf:.1f} TFLOP/s "
-            f"({tf / BF16_PEAK_TFLOPS:.1%}), step {wall_p:.3f} ms")
+            f"({tf / BF16_PEAK_TFLOPS:.1%}); writes {sum(w_layers):.3f} ms; step {wall_p:.3f} ms")
         extra["chunked_prefill_bf16"] = {
-            "layers": nl, "attn_ms": round(attn_ms, 4), "write_ms": round(w_p * nl, 4),
+            "layers": nl, "attn_ms": round(attn_ms, 4), "write_ms": round(float(sum(w_layers)), 4),
             "step_ms": round(wall_p, 4), "flops": pf.flops, "attn_TFLOPs": round(tf, 2),
             "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
-            "per_layer_attn_ms": round(a_p, 4)}
+            "per_layer_attn_ms": [round(x, 4) for x in a_layers],
+            "step_TFLOPs": round(pf.flops / (wall_p * 1e-3) / 1e12, 2)}
         result["extra"] = extra
-        del pf
+        del gp, pf
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_decode(head, args.cpu_budget)

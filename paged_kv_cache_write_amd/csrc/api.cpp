@@ -194,6 +194,8 @@ ga_status ga_attn_decode(const ga_layer_params* p, const void* q, const void* k_
   if ((int64_t)max_context_len > (int64_t)max_blocks * kPage)
     return fail(GA_ERR_INVALID_ARG, "max_context_len %d exceeds max_blocks*16 = %lld",
                 max_context_len, (long long)max_blocks * kPage);
+  if ((int64_t)batch * ((max_context_len + kPage - 1) / kPage) > 0x7fffffffLL)
+    return fail(GA_ERR_UNSUPPORTED, "batch x pages per sequence exceeds 2^31");
   const ga::DecodePlan plan = ga::plan_decode(p->head_dim, p->num_q_heads, p->num_kv_heads,
                                               p->window, batch, max_context_len,
                                               p->dtype == GA_BF16);

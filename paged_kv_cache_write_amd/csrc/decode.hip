@@ -1,0 +1,444 @@
+// decode.hip -- streamed flash decoding over the paged cache, then a merge of partial results.
+//
+// Sources: [INFLM] = "Feat/add gemma3 model" (InfiniLM pull request 581): Gemma-2 §1 (soft cap
+// of the scaled scores before the softmax), Gemma-3 §3 (a sliding decode step reads only the
+// last min(len, W) keys; head-first GQA).  [KUNLUN] = "Gemma 4 模型架构解析" §6.5 (attention
+// reads K/V through the block table).  [MNN] = "MNN 支持 Gemma4 全系列" §6.2 (K=V).
+//
+// Load balance.  The visible pages of all (sequence, kv head) segments are laid end to end and
+// cut into `nworkers` equal runs, one per single-wave worker (as many as the device holds at
+// once for this kernel, so the whole grid is resident in one round).  Ragged lengths therefore cost nothing: every worker streams the
+// same number of pages.  A worker whose run crosses segment boundaries emits one partial
+// (m, l, o) per segment piece; piece (worker w, segment s) is stored at index w + s, which is
+// unique, and the pieces of one segment are consecutive, so the merge reads a contiguous range.
+//
+// Pipelining.  A worker keeps one step (two pages; one at head size 512 or with K=V) of K and V
+// in registers: the next step's K loads are issued as soon as the current step's QK^T products
+// have consumed K, and its V loads as soon as P.V has consumed V, so global loads stay in
+// flight while the softmax and matrix-core work of the current step run.  The block ids of a
+// piece are fetched 64 at a time into one lane-register each and read back with readlane.
+#include <atomic>
+
+#include "attn_common.hpp"
+
+namespace ga {
+namespace {
+
+constexpr int kMaxWorkers = 2048;
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Inclusive wave scan of one int per lane.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+template <int D, bool KEQV>
+struct StepRegs {
+  static constexpr int NP = (KEQV || D == 512) ? 1 : 2;  // pages per step
+  u32x4_t k[NP][D / 32];
+  u32x2_t v[KEQV ? 1 : NP][KEQV ? 1 : D / 16];
+};
+
+// One piece: kv head g of sequence b, pages [pbeg, pend) (absolute page indices), visible keys
+// [lo, L).  Accumulates into acc.
+template <int D, bool CAP, bool KEQV>
+__device__ __forceinline__ void decode_piece(const AttnArgs& a, const bf16x8_t (&qf)[D / 32],
+                                             Acc<D>& acc, int b, int g, int L, int lo,
+                                             int pbeg, int pend, uint16_t* lds) {
+  using R = StepRegs<D, KEQV>;
+  constexpr int NP = R::NP, NC = D / 32, ND = D / 16;
+  const int lane = threadIdx.x & 63, c16 = lane & 15, j = lane >> 4;
+  const int64_t bt_row = (int64_t)b * a.max_blocks;
+  const int np = pend - pbeg;
+  const int nsteps = (np + NP - 1) / NP;
+  const int64_t head_off = (int64_t)g;
+
+  auto load_ids = [&](int chunk) -> int {
+    const int i = chunk * 64 + lane;
+    return i < np ? (int)clamp_blk(a.bt[bt_row + pbeg + i], a.num_blocks) : 0;
+  };
+  int ids = load_ids(0);
+  int ids_next = np > 64 ? load_ids(1) : 0;
+  int cur_chunk = 0;
+  auto ensure_chunk = [&](int rel) {
+    const int c = rel >> 6;
+    if (c != cur_chunk) {
+      ids = ids_next;
+      cur_chunk = c;
+      ids_next = (c + 1) * 64 < np ? load_ids(c + 1) : 0;
+    }
+  };
+  auto blk_of = [&](int s, int p) -> int64_t {
+    const int rel = s * NP + p;
+    const int r = rel < np ? rel : s * NP;  // a missing second page aliases the first (masked)
+    return (int64_t)__builtin_amdgcn_readlane(ids, r & 63);
+  };
+
+  // page bases are wave-uniform (scalar registers); each lane adds one 32-bit offset
+  const uint32_t koff = (uint32_t)(c16 * D + 8 * j);
+  const uint32_t voff = (uint32_t)(c16 * kPage + 4 * j);
+  const int64_t kpage = (int64_t)kPage * D;  // elements per (page, kv head)
+  R r;
+  auto issue_k = [&](int s) {
+    ensure_chunk(s * NP);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const uint16_t* kp = a.kc + (blk_of(s, p) * a.Hkv + head_off) * kpage;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) r.k[p][c] = ld16(kp + koff + 32 * c);
+    }
+  };
+  auto issue_v = [&](int s) {
+    if constexpr (!KEQV) {
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const uint16_t* vp = a.vc + (blk_of(s, p) * a.Hkv + head_off) * kpage;
+#pragma unroll
+        for (int n = 0; n < ND; ++n) r.v[p][n] = ld8(vp + voff + n * 16 * kPage);
+      }
+    }
+  };
+
+  if (nsteps > 0) {
+    issue_k(0);
+    issue_v(0);
+  }
+  for (int s = 0; s < nsteps; ++s) {
+    const int pg0 = pbeg + s * NP;              // first page of the step
+    const int k0 = pg0 * kPage;
+    const bool full = (s + 1) * NP <= np && k0 >= lo && k0 + NP * kPage <= L;
+    // S^T = K Q^T for each page of the step
+    float4_t sc[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      sc[p] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) sc[p] = mfma_16x16x32(as_bf16x8(r.k[p][c]), qf[c], sc[p]);
+    }
+    if constexpr (KEQV) {
+      // the page goes to this wave's LDS buffer for the transposed value reads
+      constexpr int S = KeqvLds<D>::kStride;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) *(u32x4_t*)(lds + c16 * S + 32 * c + 8 * j) = r.k[0][c];
+    }
+    if (s + 1 < nsteps) issue_k(s + 1);
+
+    float x[4 * NP], pr[4 * NP];
+    bool vk[4 * NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[4 * p + i] = to_log2<CAP>(sc[p][i], a.sc);
+        vk[4 * p + i] = true;
+      }
+    if (!full) {
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = k0 + p * kPage + 4 * j + i;
+          const bool ok = (s * NP + p < np) && key >= lo && key < L;
+          if (!ok) x[4 * p + i] = -INFINITY;
+          vk[4 * p + i] = ok;
+        }
+    }
+    softmax_update<D, 4 * NP>(acc, x, pr);
+
+    if constexpr (!KEQV) {
+      if constexpr (NP == 2) {
+        const bf16x8_t pf =
+            as_bf16x8(u32x4_t{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                              pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])});
+        const uint32_t mA01 = keep2(vk[0], vk[1]), mA23 = keep2(vk[2], vk[3]);
+        const uint32_t mB01 = keep2(vk[4], vk[5]), mB23 = keep2(vk[6], vk[7]);
+#pragma unroll
+        for (int n = 0; n < ND; ++n) {
+          u32x2_t va = r.v[0][n], vb = r.v[1][n];
+          if (!full) {
+            va.x &= mA01; va.y &= mA23;
+            vb.x &= mB01; vb.y &= mB23;
+          }
+          acc.o[n] = mfma_16x16x32(as_bf16x8(u32x4_t{va.x, va.y, vb.x, vb.y}), pf, acc.o[n]);
+        }
+      } else {
+        const short4_t pf = as_short4(u32x2_t{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])});
+        const uint32_t m01 = keep2(vk[0], vk[1]), m23 = keep2(vk[2], vk[3]);
+#pragma unroll
+        for (int n = 0; n < ND; ++n) {
+          u32x2_t va = r.v[0][n];
+          if (!full) { va.x &= m01; va.y &= m23; }
+          acc.o[n] = mfma_16x16x16(as_short4(va), pf, acc.o[n]);
+        }
+      }
+      if (s + 1 < nsteps) issue_v(s + 1);
+    } else {
+      constexpr int S = KeqvLds<D>::kStride;
+      const short4_t pf = as_short4(u32x2_t{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])});
+      wave_lds_sync();
+      const uint16_t* col = lds + (4 * j) * S + c16;
+#pragma unroll
+      for (int n = 0; n < ND; ++n) {
+        uint16_t e0 = col[0 * S + 16 * n], e1 = col[1 * S + 16 * n];
+        uint16_t e2 = col[2 * S + 16 * n], e3 = col[3 * S + 16 * n];
+        if (!full) {
+          e0 = vk[0] ? e0 : (uint16_t)0;
+          e1 = vk[1] ? e1 : (uint16_t)0;
+          e2 = vk[2] ? e2 : (uint16_t)0;
+          e3 = vk[3] ? e3 : (uint16_t)0;
+        }
+        const u32x2_t av = {(uint32_t)e0 | ((uint32_t)e1 << 16), (uint32_t)e2 | ((uint32_t)e3 << 16)};
+        acc.o[n] = mfma_16x16x16(as_short4(av), pf, acc.o[n]);
+      }
+      wave_lds_sync();
+    }
+  }
+}
+
+template <int D, bool CAP, bool KEQV>
+__global__ __launch_bounds__(256) void decode_stream_kernel(AttnArgs a) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  const int lane = threadIdx.x & 63, c16 = lane & 15, j = lane >> 4;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int worker = blockIdx.x * 4 + wave;
+  if (worker >= a.nworkers) return;
+  const int G = a.G, Hkv = a.Hkv, B = a.batch;
+  uint16_t* lds = (uint16_t*)smem_raw + (KEQV ? wave * KeqvLds<D>::kElems : 0);
+
+  // total visible pages over the batch (and the prefix array, written once by worker 0)
+  int64_t total = 0;
+  for (int c0 = 0; c0 < B; c0 += 64) {
+    int L, lo, p0, npg = 0;
+    if (c0 + lane < B) decode_range(a, c0 + lane, L, lo, p0, npg);
+    const int incl = wave_incl_scan(npg);
+    if (worker == 0) {
+      if (c0 == 0 && lane == 0) a.ws_pref[0] = 0;
+      if (c0 + lane < B) a.ws_pref[c0 + lane + 1] = (int)total + incl;
+    }
+    total += __builtin_amdgcn_readlane(incl, 63);
+  }
+  total *= Hkv;
+  if (total == 0) return;
+  const int64_t per = (total + a.nworkers - 1) / a.nworkers;
+  const int64_t u0 = (int64_t)worker * per;
+  const int64_t u1 = u0 + per < total ? u0 + per : total;
+  if (u0 >= u1) return;
+
+  // the sequence holding unit u0: first b with Hkv * prefix(b + 1) > u0
+  int b = 0;
+  int64_t pref = 0;
+  for (int c0 = 0; c0 < B; c0 += 64) {
+    int L, lo, p0, npg = 0;
+    if (c0 + lane < B) decode_range(a, c0 + lane, L, lo, p0, npg);
+    const int incl = wave_incl_scan(npg);
+    const uint64_t hit = __ballot((pref + incl) * Hkv > u0 && c0 + lane < B);
+    if (hit) {
+      const int f = __builtin_ctzll(hit);
+      b = c0 + f;
+      pref += __builtin_amdgcn_readlane(incl - npg, f);
+      break;
+    }
+    pref += __builtin_amdgcn_readlane(incl, 63);
+  }
+
+  bf16x8_t qf[D / 32];
+  int64_t u = u0;
+  while (u < u1 && b < B) {
+    int L, lo, p0, npg;
+    decode_range(a, b, L, lo, p0, npg);
+    const int64_t base = pref * Hkv;
+    if (npg == 0 || u >= base + (int64_t)npg * Hkv) {
+      pref += npg;
+      ++b;
+      continue;
+    }
+    const int g = (int)((u - base) / npg);
+    const int lp = (int)(u - base - (int64_t)g * npg);
+    const int64_t seg_end = base + (int64_t)(g + 1) * npg;
+    const int64_t pe_u = u1 < seg_end ? u1 : seg_end;
+    const int cnt = (int)(pe_u - u);
+
+    const bool head_ok = c16 < G;
+    load_q<D>(qf, a.q + ((int64_t)b * a.Hq + g * G + (head_ok ? c16 : 0)) * D, head_ok);
+    Acc<D> acc;
+    acc.init();
+    decode_piece<D, CAP, KEQV>(a, qf, acc, b, g, L, lo, p0 + lp, p0 + lp + cnt, lds);
+    acc.l += __shfl_xor(acc.l, 16, kWave);
+    acc.l += __shfl_xor(acc.l, 32, kWave);
+    const int64_t row = ((int64_t)worker + (int64_t)b * Hkv + g) * G + c16;
+    if (head_ok) {
+#pragma unroll
+      for (int n = 0; n < D / 16; ++n) *(float4_t*)(a.ws_o + row * D + 16 * n + 4 * j) = acc.o[n];
+      if (j == 0) *(float2*)(a.ws_ml + row * 2) = make_float2(acc.m, acc.l);
+    }
+    u = pe_u;
+  }
+}
+
+// Merge the pieces of one (sequence, query head): out = sum 2^(m_i-M) o_i / sum 2^(m_i-M) l_i.
+// Stage 1 turns every piece's (m, l) into a weight in LDS; stage 2 splits the D/4 float4
+// columns x pieces over the 256 threads so that many loads are in flight, then sums groups.
+__device__ __forceinline__ float block_reduce(float v, bool is_max, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float o = __shfl_xor(v, m, kWave);
+    v = is_max ? fmaxf(v, o) : v + o;
+  }
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
+  __syncthreads();
+  return r;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
+  constexpr int C4 = D / 4;     // float4 columns
+  constexpr int NG = 256 / C4;  // piece groups
+  __shared__ float wts[kMaxWorkers + 1];
+  __shared__ float red[4];
+  __shared__ float4_t part[256];
+  const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int G = a.G, g = h / G, hh = h - g * G;
+  uint16_t* dst = a.out + ((int64_t)b * a.Hq + h) * D;
+  const int64_t pref_b = a.ws_pref[b];
+  const int npg = a.ws_pref[b + 1] - (int)pref_b;
+  const int64_t total = (int64_t)a.ws_pref[a.batch] * a.Hkv;
+  if (npg <= 0 || total <= 0) {
+    if (t < C4) *(u32x2_t*)(dst + 4 * t) = u32x2_t{0u, 0u};
+    return;
+  }
+  const int64_t per = (total + a.nworkers - 1) / a.nworkers;
+  const int64_t start = pref_b * a.Hkv + (int64_t)g * npg;
+  const int64_t w0 = start / per, w1 = (start + npg - 1) / per;
+  const int ns = (int)(w1 - w0 + 1);
+  const int64_t row0 = (w0 + (int64_t)b * a.Hkv + g) * G + hh;  // row of piece i: row0 + i*G
+  float mloc = -INFINITY;
+  for (int i = t; i < ns; i += 256) mloc = fmaxf(mloc, a.ws_ml[(row0 + (int64_t)i * G) * 2]);
+  const float M = block_reduce(mloc, true, red);
+  float lloc = 0.f;
+  for (int i = t; i < ns; i += 256) {
+    const float2 ml = *(const float2*)(a.ws_ml + (row0 + (int64_t)i * G) * 2);
+    const float e = fast_exp2(ml.x - M);
+    wts[i] = e;
+    lloc += e * ml.y;
+  }
+  const float Lsum = block_reduce(lloc, false, red);  // its barrier also publishes wts
+  const float inv = 1.0f / Lsum;
+  const int c = t % C4, gi = t / C4;
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int i = gi; i < ns; i += NG) {
+    const float4_t v = *(const float4_t*)(a.ws_o + (row0 + (int64_t)i * G) * D + 4 * c);
+    acc += wts[i] * v;
+  }
+  part[t] = acc;
+  __syncthreads();
+  if (gi == 0) {
+#pragma unroll
+    for (int g2 = 1; g2 < NG; ++g2) acc += part[g2 * C4 + c];
+    *(u32x2_t*)(dst + 4 * c) = u32x2_t{pack_bf16x2(acc[0] * inv, acc[1] * inv),
+                                       pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+  }
+}
+
+// Resident single-wave workers the device can hold for one kernel variant: CUs x 4 SIMDs x
+// waves per SIMD (from the occupancy of 4-wave workgroups).  The answer depends only on the
+// device and the kernel, so it is computed once per (device, variant) and cached.
+template <int D, bool CAP, bool KEQV>
+int resident_workers(size_t lds) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
+  if (dev >= 0) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cus = 256, blocks = 1;
+  if (dev >= 0) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &blocks, reinterpret_cast<const void*>(&decode_stream_kernel<D, CAP, KEQV>), 256,
+          lds) != hipSuccess || blocks < 1)
+    blocks = 1;
+  int w = cus * blocks * 4;
+  w = w < 1 ? 1 : (w > kMaxWorkers ? kMaxWorkers : w);
+  if (dev >= 0) cache[dev].store(w, std::memory_order_relaxed);
+  return w;
+}
+
+template <int D, bool CAP, bool KEQV>
+hipError_t launch_t(AttnArgs a, int max_workers, hipStream_t s) {
+  const size_t lds = KEQV ? (size_t)4 * KeqvLds<D>::kElems * sizeof(uint16_t) : 0;
+  const int res = resident_workers<D, CAP, KEQV>(lds);
+  a.nworkers = res < max_workers ? res : max_workers;
+  hipLaunchKernelGGL((decode_stream_kernel<D, CAP, KEQV>), dim3((a.nworkers + 3) / 4),
+                     dim3(256), lds, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.Hq, a.batch), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t by_flags(const AttnArgs& a, int mw, bool cap, bool keqv, hipStream_t s) {
+  if (cap) return keqv ? launch_t<D, true, true>(a, mw, s) : launch_t<D, true, false>(a, mw, s);
+  return keqv ? launch_t<D, false, true>(a, mw, s) : launch_t<D, false, false>(a, mw, s);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+DecodePlan plan_decode(int D, int Hq, int Hkv, int window, int batch, int max_context_len,
+                       bool bf16) {
+  DecodePlan p{0, 0, 0, 0, 0, 0};
+  if (!bf16) return p;  // the fp32 path needs no workspace
+  int64_t pages = (max_context_len + kPage - 1) / kPage;
+  if (window > 0) {
+    const int64_t wp = (int64_t)window / kPage + 2;  // a window can straddle one extra page
+    if (wp < pages) pages = wp;
+  }
+  if (pages < 1) pages = 1;
+  // at most kMaxWorkers single-wave workers (the launch uses as many as are resident), and
+  // never more workers than pages
+  const int64_t units = (int64_t)batch * Hkv * pages;
+  p.nworkers = (int)(units < kMaxWorkers ? units : kMaxWorkers);
+  if (p.nworkers < 1) p.nworkers = 1;
+  const int G = Hq / Hkv;
+  p.npieces = (int64_t)p.nworkers + (int64_t)batch * Hkv;
+  p.pref_bytes = align256((size_t)(batch + 1) * sizeof(int32_t));
+  p.ml_bytes = align256((size_t)p.npieces * G * 2 * sizeof(float));
+  p.o_bytes = align256((size_t)p.npieces * G * D * sizeof(float));
+  p.workspace_bytes = p.pref_bytes + p.ml_bytes + p.o_bytes;
+  return p;
+}
+
+hipError_t launch_decode(const AttnLaunch& L, const DecodePlan& plan, hipStream_t s) {
+  if (L.batch == 0) return hipSuccess;
+  if (!L.dtype_bf16) return launch_attn_f32(L, true, s);
+  AttnArgs a = make_attn_args(L);
+  unsigned char* ws = (unsigned char*)L.workspace;
+  a.ws_pref = (int32_t*)ws;
+  a.ws_ml = (float*)(ws + plan.pref_bytes);
+  a.ws_o = (float*)(ws + plan.pref_bytes + plan.ml_bytes);
+  const bool cap = L.softcap > 0.f, keqv = L.k_eq_v != 0;
+  switch (L.D) {
+    case 128: return by_flags<128>(a, plan.nworkers, cap, keqv, s);
+    case 256: return by_flags<256>(a, plan.nworkers, cap, keqv, s);
+    case 512: return by_flags<512>(a, plan.nworkers, cap, keqv, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ga

@@ -46,10 +46,11 @@ struct AttnLaunch {
   void* workspace;
 };
 
-// Split-K plan of a decode call; a pure function of the host arguments.
+// Decode launch plan; a pure function of the host arguments.
 struct DecodePlan {
-  int pages_per_split;  // multiple of 8
-  int num_splits;       // splits of the longest visible key range
+  int nworkers;           // upper bound on the single-wave workers of one launch
+  int64_t npieces;        // upper bound on (worker, sequence x kv head) pieces
+  size_t pref_bytes, ml_bytes, o_bytes;  // workspace regions (256-byte aligned)
   size_t workspace_bytes;
 };
 
@@ -59,5 +60,6 @@ DecodePlan plan_decode(int D, int Hq, int Hkv, int window, int batch, int max_co
 hipError_t launch_kv_write(const KvWriteLaunch& a, hipStream_t s);
 hipError_t launch_decode(const AttnLaunch& a, const DecodePlan& plan, hipStream_t s);
 hipError_t launch_prefill(const AttnLaunch& a, hipStream_t s);
+hipError_t launch_attn_f32(const AttnLaunch& a, bool decode, hipStream_t s);
 
 }  // namespace ga

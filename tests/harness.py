@@ -122,13 +122,17 @@ def assert_attn_close(got: torch.Tensor, ref: np.ndarray, dtype: str, rows=None,
     return mx, mean
 
 
-def assert_within_bf16_ulps(a: torch.Tensor, b: torch.Tensor, ulps: int = 2):
-    """Two bf16 results of the same math that differ only in summation order: each element
-    within `ulps` units in the last place of the larger magnitude (bf16 keeps 8 bits)."""
-    x, y = a.float().cpu(), b.float().cpu()
-    tol = ulps * torch.maximum(x.abs(), y.abs()) * 2.0 ** -7 + 1e-6
-    bad = (x - y).abs() > tol
-    assert not bad.any(), f"{int(bad.sum())} elements differ by more than {ulps} ulps"
+def assert_same_result(a: torch.Tensor, b: torch.Tensor, dtype: str = "bf16"):
+    """Two GPU results of the same attention computed with a different partition of the work
+    (decode vs prefill rows, K=V vs a copied V cache, GQA vs repeated heads): each is within the
+    parity bar of the exact value, so they are held to that bar against each other."""
+    x, y = a.float().cpu().numpy().astype(np.float64), b.float().cpu().numpy().astype(np.float64)
+    err = np.abs(x - y)
+    if dtype == "bf16":
+        assert err.max() <= BF16_MAX_ABS and err.mean() <= BF16_MEAN_ABS, \
+            f"max {err.max():.3e} mean {err.mean():.3e}"
+    else:
+        assert err.max() <= FP32_MAX_ABS, f"max {err.max():.3e}"
 
 
 def ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
