@@ -75,59 +75,6 @@ __device__ __forceinline__ uint32_t keep2(bool a, bool b) {
   return (a ? 0x0000ffffu : 0u) | (b ? 0xffff0000u : 0u);
 }
 
-// One wave step over two pages A, B (32 keys) with separate K and V caches.
-//   kA/kB: K row pointers already offset to (row c16, column 8j); vA/vB: V^T page pointers
-//   offset to (d row c16, key 4j); keyA/keyB: absolute key of slot 0 (= page*16 + 4j);
-//   [lo_c, hi_c]: keys visible to this lane's row; [vlo, vhi): keys whose V may be read.
-template <int D, bool CAP, bool MASKED>
-__device__ __forceinline__ void step_kv2(Acc<D>& acc, const bf16x8_t (&qf)[D / 32],
-                                         const uint16_t* kA, const uint16_t* kB,
-                                         const uint16_t* vA, const uint16_t* vB, int keyA,
-                                         int keyB, bool b_ok, int lo_c, int hi_c, int vlo,
-                                         int vhi, const ScoreConsts& k) {
-  float4_t sA = {0.f, 0.f, 0.f, 0.f}, sB = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int c = 0; c < D / 32; ++c) {
-    sA = mfma_16x16x32(as_bf16x8(ld16(kA + 32 * c)), qf[c], sA);
-    sB = mfma_16x16x32(as_bf16x8(ld16(kB + 32 * c)), qf[c], sB);
-  }
-  float x[8], p[8];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    x[r] = to_log2<CAP>(sA[r], k);
-    x[4 + r] = to_log2<CAP>(sB[r], k);
-  }
-  uint32_t mA01 = ~0u, mA23 = ~0u, mB01 = ~0u, mB23 = ~0u;
-  if constexpr (MASKED) {
-    bool va[4], vb[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int ka = keyA + r, kb = keyB + r;
-      if (!(ka >= lo_c && ka <= hi_c)) x[r] = -INFINITY;
-      if (!(b_ok && kb >= lo_c && kb <= hi_c)) x[4 + r] = -INFINITY;
-      va[r] = ka >= vlo && ka < vhi;
-      vb[r] = b_ok && kb >= vlo && kb < vhi;
-    }
-    mA01 = keep2(va[0], va[1]);
-    mA23 = keep2(va[2], va[3]);
-    mB01 = keep2(vb[0], vb[1]);
-    mB23 = keep2(vb[2], vb[3]);
-  }
-  softmax_update<D, 8>(acc, x, p);
-  const bf16x8_t pf = as_bf16x8(u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                        pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])});
-#pragma unroll
-  for (int n = 0; n < D / 16; ++n) {
-    u32x2_t a = ld8(vA + n * 16 * kPage);
-    u32x2_t b = ld8(vB + n * 16 * kPage);
-    if constexpr (MASKED) {
-      a.x &= mA01; a.y &= mA23;
-      b.x &= mB01; b.y &= mB23;
-    }
-    acc.o[n] = mfma_16x16x32(as_bf16x8(u32x4_t{a.x, a.y, b.x, b.y}), pf, acc.o[n]);
-  }
-}
-
 // Row stride (elements) of a wave's LDS page buffer in the K=V path: 16 bytes of padding
 // shift consecutive rows by 4 banks so the column-wise reads of 4 rows hit distinct banks.
 template <int D>
@@ -140,52 +87,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
-
-// One wave step over one page (16 keys) whose K rows also serve as V (k_eq_v).
-template <int D, bool CAP, bool MASKED>
-__device__ __forceinline__ void step_keqv1(Acc<D>& acc, const bf16x8_t (&qf)[D / 32],
-                                           const uint16_t* kp, uint16_t* lds, int key0,
-                                           int lo_c, int hi_c, int vlo, int vhi,
-                                           const ScoreConsts& k) {
-  constexpr int S = KeqvLds<D>::kStride;
-  const int lane = threadIdx.x & 63, c16 = lane & 15, j = lane >> 4;
-  float4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int c = 0; c < D / 32; ++c) {
-    const u32x4_t kv = ld16(kp + 32 * c);
-    *(u32x4_t*)(lds + c16 * S + 32 * c + 8 * j) = kv;
-    s = mfma_16x16x32(as_bf16x8(kv), qf[c], s);
-  }
-  float x[4], p[4];
-  bool vk[4] = {true, true, true, true};
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    x[r] = to_log2<CAP>(s[r], k);
-    if constexpr (MASKED) {
-      const int kk = key0 + r;
-      if (!(kk >= lo_c && kk <= hi_c)) x[r] = -INFINITY;
-      vk[r] = kk >= vlo && kk < vhi;
-    }
-  }
-  softmax_update<D, 4>(acc, x, p);
-  const short4_t pf = as_short4(u32x2_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])});
-  wave_lds_sync();
-  const uint16_t* col = lds + (4 * j) * S + c16;
-#pragma unroll
-  for (int n = 0; n < D / 16; ++n) {
-    uint16_t e0 = col[0 * S + 16 * n], e1 = col[1 * S + 16 * n];
-    uint16_t e2 = col[2 * S + 16 * n], e3 = col[3 * S + 16 * n];
-    if constexpr (MASKED) {
-      e0 = vk[0] ? e0 : (uint16_t)0;
-      e1 = vk[1] ? e1 : (uint16_t)0;
-      e2 = vk[2] ? e2 : (uint16_t)0;
-      e3 = vk[3] ? e3 : (uint16_t)0;
-    }
-    const u32x2_t a = {(uint32_t)e0 | ((uint32_t)e1 << 16), (uint32_t)e2 | ((uint32_t)e3 << 16)};
-    acc.o[n] = mfma_16x16x16(as_short4(a), pf, acc.o[n]);
-  }
-  wave_lds_sync();
 }
 
 __device__ __forceinline__ int64_t clamp_blk(int64_t blk, int64_t nb) {

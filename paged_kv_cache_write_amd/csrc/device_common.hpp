@@ -19,6 +19,8 @@
 namespace ga {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float float2_t;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
 typedef __attribute__((ext_vector_type(4))) short short4_t;
 typedef __attribute__((ext_vector_type(4))) float float4_t;
@@ -47,6 +49,17 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // Two fp32 -> packed bf16x2 (lo in bits 0..15), round to nearest even.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Two fp32 -> bf16x2 with the hardware conversion (round to nearest even).
+__device__ __forceinline__ bf16x2_t cvt_bf16x2(float lo, float hi) {
+  return __builtin_convertvector(float2_t{lo, hi}, bf16x2_t);
+}
+
+// acc + w.x + w.y in fp32 (one dot-product instruction).
+__device__ __forceinline__ float sum_bf16x2(bf16x2_t w, float acc) {
+  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(w, one, acc, false);
 }
 
 // double -> bf16 with a single rounding (nearest, ties to even): round to fp32 toward zero,
@@ -83,6 +96,16 @@ __device__ __forceinline__ short4_t as_short4(const u32x2_t& v) {
 
 __device__ __forceinline__ float xor_max(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, kWave));
+}
+// Max over the 4 lane groups (lanes c, c+16, c+32, c+48) without LDS: the two permlane swaps
+// exchange rows of 16 and halves of 32 lanes.
+__device__ __forceinline__ float max_over_groups(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  v = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  const uint32_t w = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll

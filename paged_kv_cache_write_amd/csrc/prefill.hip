@@ -1,0 +1,461 @@
+// prefill.hip -- chunked-prefill flash attention over the paged cache (bf16, matrix cores).
+//
+// Sources: [INFLM] = "Feat/add gemma3 model" (InfiniLM pull request 581): Gemma-2 §1 (soft cap
+// of the scaled scores before mask and softmax), Gemma-3 §3 (query i of a chunk appended after
+// `past` cached tokens sees key j when j <= past + i and, on a sliding layer, past + i - j < W;
+// this holds for chunked prefill; head-first GQA) and its follow-up list (only keys inside the
+// window need to be visited).  [KUNLUN] = "Gemma 4 模型架构解析" §6.5 (K/V read through the
+// block table).  [MNN] = "MNN 支持 Gemma4 全系列" §6.2 (K=V).
+//
+// Tiling.  A workgroup of 8 waves (two per SIMD, so one wave's softmax and LDS latency hide
+// behind the other's matrix-core work) owns 256 rows (128 at head size 512) of one (sequence,
+// kv head): rows are (position, query head) pairs ordered position-major, so the G heads of a
+// GQA group share every key tile.  Each wave holds 32 rows (two 16-column MFMA blocks; 16 rows
+// at head size 512) with Q^T and the O^T accumulators in registers.  Key tiles of 32 keys (two
+// pages) are copied from HBM straight into LDS by global_load_lds_dwordx4 (no registers
+// involved) through a ring of up to 4 stages of K and V^T tiles; one barrier per tile both
+// publishes a tile and frees a stage.  Only tiles that intersect the band
+// [past + i - W + 1, past + i] of some row are visited; tiles whose every key is visible to
+// every row of a wave skip all masking.  Keys past the context (only in the last tile) are
+// zeroed in LDS once, so no value read needs a mask.
+//
+// Key order inside a tile.  The 16 rows of the first QK^T product of a tile are keys
+// {0-3, 8-11} of each of its two pages and the second product's rows are keys {4-7, 12-15},
+// so that the four scores lane group j receives from each product are 8 consecutive keys of
+// one page (page j/2, keys 8(j%2) .. 8(j%2)+7).  The probabilities then form the P^T operand
+// of P.V without moving between lanes, and the matching V^T operand is one 16-byte read.
+//
+// LDS layouts (per page of 16 keys), chosen so that every operand read is one base register
+// plus an immediate offset, is free of bank conflicts, and still arrives as whole 16-byte
+// pieces from HBM:
+//   K page  chunk-major: the 16-byte chunk x (elements 8x .. 8x+7) of key row r of page p is
+//           stored at byte 256 x + 16 ((r + 4p) mod 16), so a QK^T fragment read by 16 lanes
+//           (16 distinct rows, one chunk) covers 16 distinct bank groups.
+//   V^T page [D rows][16 keys] (32 bytes a row): the two 16-byte halves of row d are swapped
+//           when bit 3 of d is set.
+// Block ids of the workgroup's pages are staged in LDS once per pass, so the loop issues no
+// vector-memory operation except the tile copies, whose completion it counts exactly.
+//
+// Order of work: workgroup ids are dealt to the 8 XCDs round robin, so consecutive logical
+// tiles are given to one XCD (its L2 then serves the key tiles shared by neighbouring row
+// tiles), and within a (sequence, kv head) the row tiles with the most keys start first.
+#include "attn_common.hpp"
+
+namespace ga {
+namespace {
+
+constexpr int kTileKeys = 2 * kPage;  // 32 keys per tile: P.V runs on 16x16x32 MFMAs
+constexpr int kWaves = 8;             // two waves per SIMD, 256 registers each
+constexpr int kMaxIds = 1024;         // block ids staged per pass (512 tiles, 16384 keys)
+
+// MFMA column blocks per wave: 2 (32 rows) up to head size 256, 1 (16 rows) at 512, where
+// 32 rows of Q^T (128 registers) plus O^T (256) would not fit a wave's 256 registers.
+template <int D>
+struct Rows {
+  static constexpr int kR = D == 512 ? 1 : 2;
+  static constexpr int kPerWave = 16 * kR;
+  static constexpr int kPerWg = kWaves * kPerWave;
+};
+
+// LDS: a ring of K tiles and a ring of V^T tiles (K=V: the K ring only), then the block ids.
+template <int D, bool KEQV>
+struct TileLds {
+  static constexpr int kPageBytes = kPage * D * 2;  // one page of K (or V^T)
+  static constexpr int kTile = 2 * kPageBytes;      // one 32-key tile of K (or of V^T)
+  static constexpr int kBudget = 128 * 1024;
+  static constexpr int kPerStage = KEQV ? kTile : 2 * kTile;
+  static constexpr int kStages = kBudget / kPerStage >= 4 ? 4 : kBudget / kPerStage;
+  static constexpr int kKRing = 0;
+  static constexpr int kVRing = kStages * kTile;
+  static constexpr int kIds = kStages * kPerStage;
+  static constexpr int kBytes = kIds + kMaxIds * 4;
+  static constexpr int kChunks = kTile / 1024;          // 1 KiB copies per tile
+  static constexpr int kPerWave = kChunks / kWaves;     // copies per wave per tile
+  static_assert(kChunks % kWaves == 0, "tile copies split evenly over the waves");
+};
+
+// Row of page c16 / 8 that QK^T product m (0, 1) places at MFMA row c16: keys {0-3, 8-11} of
+// each page for m = 0 and {4-7, 12-15} for m = 1.
+__device__ __forceinline__ int qk_row_key(int c16, int m) {
+  return (c16 & 3) + 8 * ((c16 >> 2) & 1) + 4 * m;
+}
+
+// One HBM -> LDS copy of 1 KiB: each lane moves 16 bytes to M0 + 16 * lane.  Issued through
+// inline assembly so that the compiler does not add waits of its own for the LDS it writes:
+// the kernel waits on the vector-memory counter explicitly before the barrier that
+// publishes a tile.
+__device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_off)
+               : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Copies of one tile of K (V=false) or of V^T (V=true) into `lds_off`.
+template <int D, bool KEQV, bool V>
+__device__ __forceinline__ void issue_tile(const AttnArgs& a, uint32_t lds_off, int g,
+                                           int64_t blkA, int64_t blkB, int wave, int lane) {
+  using T = TileLds<D, KEQV>;
+  constexpr int kChunksPerPage = T::kPageBytes / 1024;
+#pragma unroll
+  for (int i = 0; i < T::kPerWave; ++i) {
+    const int q = wave + kWaves * i;  // 1 KiB chunk of the tile
+    const int page = q / kChunksPerPage, qq = q - page * kChunksPerPage;
+    const int s = qq * 64 + lane;     // 16-byte slot inside the page
+    const int64_t blk = page ? blkB : blkA;
+    const void* src;
+    if constexpr (!V) {
+      const int x = s >> 4, r = ((s & 15) - 4 * page) & 15;  // chunk-major, rotated by 4 page
+      src = a.kc + ((blk * a.Hkv + g) * kPage + r) * D + x * 8;
+    } else {
+      const int d = s >> 1, h = (s & 1) ^ ((d >> 3) & 1);
+      src = a.vc + ((blk * a.Hkv + g) * D + d) * kPage + h * 8;
+    }
+    lds_copy16(src, __builtin_amdgcn_readfirstlane(lds_off + q * 1024));
+  }
+}
+
+// Zero, in one staged tile, the values of key slots nvalid .. 31 (keys past the context):
+// the V^T pages (or, K=V, the K pages, which then serve as values).  All threads take part.
+template <int D, bool KEQV>
+__device__ __forceinline__ void zero_tail_values(unsigned char* tile, int nvalid) {
+  using T = TileLds<D, KEQV>;
+  if constexpr (!KEQV) {
+    // V^T page [D rows][16 keys]: one row (32 bytes) of one page per step
+    for (int q = threadIdx.x; q < 2 * D; q += 64 * kWaves) {
+      const int page = q / D, d = q - page * D;
+      unsigned char* row = tile + page * T::kPageBytes + d * 32;
+#pragma unroll
+      for (int r = 0; r < kPage; ++r)
+        if (page * kPage + r >= nvalid)
+          *(uint16_t*)(row + 16 * ((r >> 3) ^ ((d >> 3) & 1)) + 2 * (r & 7)) = 0;
+    }
+  } else {
+    // chunk-major K page: 16-byte unit (row r, chunk x) at 256 x + 16 ((r + 4 page) mod 16)
+    for (int q = threadIdx.x; q < 2 * kPage * (D / 8); q += 64 * kWaves) {
+      const int page = q / (kPage * (D / 8)), u = q - page * (kPage * (D / 8));
+      const int x = u >> 4, r = u & 15;
+      if (page * kPage + r >= nvalid)
+        *(u32x4_t*)(tile + page * T::kPageBytes + 256 * x + 16 * ((r + 4 * page) & 15)) =
+            u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+template <int D, bool CAP, bool KEQV>
+__global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs a, int tiles_per_bg,
+                                                                     int n_tiles) {
+  using T = TileLds<D, KEQV>;
+  constexpr int NC = D / 32, ND = D / 16, R = Rows<D>::kR, S = T::kStages;
+  constexpr int kRowsPerWave = Rows<D>::kPerWave, kRowsPerWg = Rows<D>::kPerWg;
+  static_assert(S >= 2 && S <= 4, "ring depth");
+  extern __shared__ __align__(16) unsigned char smem[];
+  const uint32_t smem_off =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+  int* ids = (int*)(smem + T::kIds);
+  const int lane = threadIdx.x & 63, c16 = lane & 15, j = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  // ---- which (sequence, kv head, row tile) this workgroup owns (XCD-contiguous order):
+  // the grid is a multiple of 8, so this is a bijection of [0, gridDim.x); the padding returns
+  const int per_xcd = gridDim.x / 8;
+  const int logical = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (logical >= n_tiles) return;
+  const int bg = logical / tiles_per_bg;
+  const int rt = tiles_per_bg - 1 - (logical - bg * tiles_per_bg);  // most keys first
+  const int b = bg / a.Hkv, g = bg - (bg / a.Hkv) * a.Hkv;
+  if (b >= a.batch) return;
+  const int G = a.G, W = a.window;
+  const int q0 = a.cu[b];
+  int n = a.cu[b + 1] - q0;
+  n = n > a.max_q_len ? a.max_q_len : n;
+  n = n > a.total_q - q0 ? a.total_q - q0 : n;
+  int L = a.ctx[b];
+  L = L > a.max_ctx ? a.max_ctx : L;
+  const int past = L - n;
+  const int row0 = rt * kRowsPerWg;
+  if (q0 < 0 || n <= 0 || past < 0 || row0 >= n * G) return;  // uniform over the workgroup
+
+  // ---- key tiles of the workgroup: keys [lo(first row), position(last row)]
+  const int nrows_wg = (n * G - row0) < kRowsPerWg ? (n * G - row0) : kRowsPerWg;
+  const int t_first_wg = past + row0 / G, t_last_wg = past + (row0 + nrows_wg - 1) / G;
+  const int lo_first_wg = W > 0 ? (t_first_wg - W + 1 > 0 ? t_first_wg - W + 1 : 0) : 0;
+  const int kt0 = lo_first_wg / kTileKeys, kt1 = t_last_wg / kTileKeys;  // inclusive
+  const int ntiles = kt1 - kt0 + 1;
+
+  // ---- this wave's rows
+  const int wrow0 = row0 + wave * kRowsPerWave;
+  const int wrows = (n * G - wrow0) < kRowsPerWave ? (n * G - wrow0) : kRowsPerWave;
+  // Row rb of this lane sees key k iff (unsigned)(k - lo_c[rb]) <= span_c[rb], i.e.
+  // lo <= k <= position; padding rows see nothing.
+  int lo_c[R];
+  uint32_t span_c[R];
+  bool ok_c[R];
+  bf16x8_t qf[R][NC];
+#pragma unroll
+  for (int rb = 0; rb < R; ++rb) {
+    const int rr = 16 * rb + c16;
+    ok_c[rb] = rr < wrows;
+    const int row = wrow0 + (ok_c[rb] ? rr : 0);
+    const int i = row / G, hh = row - (row / G) * G;
+    const int t = past + i;
+    const int lo = W > 0 ? (t - W + 1 > 0 ? t - W + 1 : 0) : 0;
+    lo_c[rb] = ok_c[rb] ? lo : (1 << 30);
+    span_c[rb] = ok_c[rb] ? (uint32_t)(t - lo) : 0u;
+    load_q<D>(qf[rb], a.q + ((int64_t)(q0 + i) * a.Hq + g * G + hh) * D, ok_c[rb]);
+  }
+  // wave-uniform bounds: union [vlo, vhi] and intersection [lo_max, hi_min] of the rows' ranges
+  const bool wave_active = wrows > 0;
+  const int t_first_w = past + (wave_active ? wrow0 : row0) / G;
+  const int t_last_w = past + (wave_active ? wrow0 + wrows - 1 : row0) / G;
+  const int vlo = W > 0 ? (t_first_w - W + 1 > 0 ? t_first_w - W + 1 : 0) : 0;
+  const int vhi = t_last_w;
+  const int lo_max = W > 0 ? (t_last_w - W + 1 > 0 ? t_last_w - W + 1 : 0) : 0;
+  const int hi_min = t_first_w;
+
+  float m_ref[R], l_run[R];
+  float4_t o[R][ND];
+#pragma unroll
+  for (int rb = 0; rb < R; ++rb) {
+    m_ref[rb] = -INFINITY;
+    l_run[rb] = 0.f;
+#pragma unroll
+    for (int nn = 0; nn < ND; ++nn) o[rb][nn] = float4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int64_t bt_row = (int64_t)b * a.max_blocks;
+  const int last_page = (L - 1) / kPage;
+
+  // Lane offsets inside a tile (bytes); fragment c / column block nn adds an immediate.
+  //   K, product m: row qk_row_key(c16, m) of page c16 / 8, chunk 4c + j.
+  //   V^T: row d = 16 nn + c16 of page j / 2, the 8 keys 8 (j % 2) .. + 7.
+  const int kpage = c16 >> 3;
+  int koff[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+    koff[m] = kpage * T::kPageBytes + 256 * j + 16 * ((qk_row_key(c16, m) + 4 * kpage) & 15);
+  const int voff = (j >> 1) * T::kPageBytes + c16 * 32 + (((j & 1) ^ ((c16 >> 3) & 1)) * 16);
+  // key of score slot e (product e / 4, register e % 4) of this lane group, minus k0
+  const int kslot = (j >> 1) * kPage + 8 * (j & 1);
+
+  constexpr int kPerIt = T::kPerWave * (KEQV ? 1 : 2);
+  for (int pass0 = 0; pass0 < ntiles; pass0 += kMaxIds / 2) {
+    const int np = (ntiles - pass0) < kMaxIds / 2 ? (ntiles - pass0) : kMaxIds / 2;
+    // ---- block ids of this pass's pages, staged once (nothing else is in flight here)
+    __syncthreads();  // the previous pass is done with the id table
+    for (int i = threadIdx.x; i < 2 * np; i += 64 * kWaves) {
+      const int page = 2 * (kt0 + pass0) + i;
+      ids[i] = page <= last_page ? (int)clamp_blk(a.bt[bt_row + page], a.num_blocks) : -1;
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    auto issue = [&](int it) {
+      const int iA = ids[2 * it], iB = ids[2 * it + 1];
+      const int64_t bA = iA, bB = iB >= 0 ? iB : iA;  // past the last page: alias the first
+      issue_tile<D, KEQV, false>(a, smem_off + T::kKRing + (it % S) * T::kTile, g, bA, bB,
+                                 wave, lane);
+      if constexpr (!KEQV)
+        issue_tile<D, KEQV, true>(a, smem_off + T::kVRing + (it % S) * T::kTile, g, bA, bB,
+                                  wave, lane);
+    };
+
+    // Prologue: tiles 0..S-2.  Iteration it consumes tile it and, after the barrier that
+    // proves every wave has left iteration it-1, refills that iteration's stage with tile
+    // it+S-1.
+    for (int u = 0; u < S - 1; ++u)
+      if (u < np) issue(u);
+
+    for (int it = 0; it < np; ++it) {
+      // Tile it must have landed.  In steady state the copies issued after it are those of
+      // the last S-2 iterations; once the issues stop (tail) everything is waited for.
+      {
+        const bool tail = it + S - 1 > np;
+        const int after = tail ? 0 : (it < S - 2 ? it : S - 2);
+        if (after >= 2) wait_vmcnt<2 * kPerIt>();
+        else if (after == 1) wait_vmcnt<kPerIt>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+      }
+      if (it + S - 1 < np) issue(it + S - 1);
+
+      const int k0 = (kt0 + pass0 + it) * kTileKeys;
+      if (k0 + kTileKeys > L) {
+        // Last tile: slots of keys >= L may hold anything, NaN included, and a zero weight
+        // does not cancel a NaN value.  Zero the values of those keys once, in LDS.
+        zero_tail_values<D, KEQV>(smem + (it % S) * (KEQV ? T::kTile : 0) +
+                                      (KEQV ? T::kKRing : T::kVRing + (it % S) * T::kTile),
+                                  L - k0);
+        __syncthreads();
+      }
+      if (!wave_active || k0 > vhi || k0 + kTileKeys - 1 < vlo) continue;  // wave-uniform
+      const unsigned char* kt = smem + T::kKRing + (it % S) * T::kTile;
+
+      // ---- S^T = K Q^T: s[m][rb], product m covering the key rows described above
+      float4_t s[2][R];
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int rb = 0; rb < R; ++rb) s[m][rb] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const bf16x8_t kf = as_bf16x8(*(const u32x4_t*)(kt + koff[m] + 1024 * c));
+#pragma unroll
+          for (int rb = 0; rb < R; ++rb) s[m][rb] = mfma_16x16x32(kf, qf[rb][c], s[m][rb]);
+        }
+
+      // ---- scores on the log2 scale, band + causal mask (skipped when the whole tile is
+      // visible to every row of the wave)
+      const bool full = k0 >= lo_max && k0 + kTileKeys - 1 <= hi_min;
+      float xs[R][8];
+#pragma unroll
+      for (int rb = 0; rb < R; ++rb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xs[rb][e] = to_log2<CAP>(s[e >> 2][rb][e & 3], a.sc);
+      if (!full) {
+        const int kk = k0 + kslot;
+#pragma unroll
+        for (int rb = 0; rb < R; ++rb) {
+          const int d0 = kk - lo_c[rb];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            xs[rb][e] = (uint32_t)(d0 + e) <= span_c[rb] ? xs[rb][e] : -INFINITY;
+        }
+      }
+      // ---- online softmax with a lazily moved reference: the reference moves only when a
+      // weight would exceed 2^8, so most tiles skip the rescale of O
+      bool need = false;
+      float mx[R];
+#pragma unroll
+      for (int rb = 0; rb < R; ++rb) {
+        float m = fmaxf(fmaxf(fmaxf(xs[rb][0], xs[rb][1]), fmaxf(xs[rb][2], xs[rb][3])),
+                        fmaxf(fmaxf(xs[rb][4], xs[rb][5]), fmaxf(xs[rb][6], xs[rb][7])));
+        m = max_over_groups(m);
+        mx[rb] = m;
+        need |= m > m_ref[rb] + 8.0f;
+      }
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+        for (int rb = 0; rb < R; ++rb) {
+          const float m_new = mx[rb] > m_ref[rb] + 8.0f ? mx[rb] : m_ref[rb];
+          const float alpha = m_ref[rb] == -INFINITY ? 1.f : fast_exp2(m_ref[rb] - m_new);
+          l_run[rb] *= alpha;
+#pragma unroll
+          for (int nn = 0; nn < ND; ++nn) o[rb][nn] *= alpha;
+          m_ref[rb] = m_new;
+        }
+      }
+      bf16x8_t pf[R];
+#pragma unroll
+      for (int rb = 0; rb < R; ++rb) {
+        const float mu = m_ref[rb] == -INFINITY ? 0.f : m_ref[rb];
+        bf16x2_t pw[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          pw[w] = cvt_bf16x2(fast_exp2(xs[rb][2 * w] - mu), fast_exp2(xs[rb][2 * w + 1] - mu));
+          // the row sum uses the same bf16-rounded weights that multiply V
+          l_run[rb] = sum_bf16x2(pw[w], l_run[rb]);
+        }
+        pf[rb] = bf16x8_t{pw[0][0], pw[0][1], pw[1][0], pw[1][1],
+                          pw[2][0], pw[2][1], pw[3][0], pw[3][1]};
+      }
+
+      // ---- O^T[d][row] += V^T[d][keys] P^T[keys][row]
+      if constexpr (!KEQV) {
+        const unsigned char* vp = smem + T::kVRing + (it % S) * T::kTile + voff;
+#pragma unroll
+        for (int nn = 0; nn < ND; ++nn) {
+          const bf16x8_t af = as_bf16x8(*(const u32x4_t*)(vp + nn * 512));
+#pragma unroll
+          for (int rb = 0; rb < R; ++rb) o[rb][nn] = mfma_16x16x32(af, pf[rb], o[rb][nn]);
+        }
+      } else {
+        // values are the keys: gather K[key][d] column-wise from the chunk-major K page;
+        // key 8 (j % 2) + e of page j / 2 at d = 16 nn + c16
+        const int pg = j >> 1;
+        const int kb = pg * T::kPageBytes + 256 * (c16 >> 3) + 2 * (c16 & 7);
+        const int rot = 8 * (j & 1) + 4 * pg;
+#pragma unroll
+        for (int nn = 0; nn < ND; ++nn) {
+          uint32_t w[4];
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const unsigned char* p0 = kt + kb + 512 * nn + 16 * ((rot + 2 * e2) & 15);
+            const unsigned char* p1 = kt + kb + 512 * nn + 16 * ((rot + 2 * e2 + 1) & 15);
+            w[e2] = (uint32_t)(*(const uint16_t*)p0) | ((uint32_t)(*(const uint16_t*)p1) << 16);
+          }
+          const bf16x8_t af = as_bf16x8(u32x4_t{w[0], w[1], w[2], w[3]});
+#pragma unroll
+          for (int rb = 0; rb < R; ++rb) o[rb][nn] = mfma_16x16x32(af, pf[rb], o[rb][nn]);
+        }
+      }
+    }
+  }
+
+  if (!wave_active) return;
+#pragma unroll
+  for (int rb = 0; rb < R; ++rb) {
+    float l = l_run[rb];
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    if (!ok_c[rb]) continue;
+    const int row = wrow0 + 16 * rb + c16;
+    const int i = row / G, hh = row - (row / G) * G;
+    const float inv = 1.0f / l;
+    uint16_t* dst = a.out + ((int64_t)(q0 + i) * a.Hq + g * G + hh) * D + 4 * j;
+#pragma unroll
+    for (int nn = 0; nn < ND; ++nn)
+      *(u32x2_t*)(dst + 16 * nn) =
+          u32x2_t{pack_bf16x2(o[rb][nn][0] * inv, o[rb][nn][1] * inv),
+                  pack_bf16x2(o[rb][nn][2] * inv, o[rb][nn][3] * inv)};
+  }
+}
+
+template <int D, bool CAP, bool KEQV>
+hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
+  using T = TileLds<D, KEQV>;
+  constexpr int kRowsPerWg = Rows<D>::kPerWg;
+  const int tiles_per_bg = (a.max_q_len * a.G + kRowsPerWg - 1) / kRowsPerWg;
+  const int n_tiles = tiles_per_bg * a.Hkv * a.batch;
+  if (n_tiles == 0) return hipSuccess;
+  const int grid = (n_tiles + 7) / 8 * 8;  // whole rounds over the 8 XCDs
+  static_assert(T::kBytes <= 160 * 1024, "LDS budget");
+  hipError_t e = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&prefill_tiled_kernel<D, CAP, KEQV>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, T::kBytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((prefill_tiled_kernel<D, CAP, KEQV>), dim3(grid), dim3(64 * kWaves),
+                     T::kBytes, s, a, tiles_per_bg, n_tiles);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t by_flags(const AttnArgs& a, bool cap, bool keqv, hipStream_t s) {
+  if (cap) return keqv ? launch_t<D, true, true>(a, s) : launch_t<D, true, false>(a, s);
+  return keqv ? launch_t<D, false, true>(a, s) : launch_t<D, false, false>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const AttnLaunch& L, hipStream_t s) {
+  if (L.batch == 0 || L.total_q == 0) return hipSuccess;
+  if (!L.dtype_bf16) return launch_attn_f32(L, false, s);
+  const AttnArgs a = make_attn_args(L);
+  const bool cap = L.softcap > 0.f, keqv = L.k_eq_v != 0;
+  switch (L.D) {
+    case 128: return by_flags<128>(a, cap, keqv, s);
+    case 256: return by_flags<256>(a, cap, keqv, s);
+    case 512: return by_flags<512>(a, cap, keqv, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ga
