@@ -16,6 +16,7 @@ back-to-back calls between two HIP events on the launch stream.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -34,6 +35,46 @@ import workloads as wl  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
 BS = wl.BLOCK_SIZE
+
+
+# Sources of the decode kernels: the HBM traffic recorded under profiles/ applies only while
+# their hash is unchanged.
+DECODE_SOURCES = ("decode.hip", "attn_common.hpp", "device_common.hpp", "launch.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_stream_kernel.softcap_decode_bf16.pmc.md")
+
+
+def decode_sources_sha256():
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_write_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per attn_decode call of the headline workload from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by the copy-kernel calibration), or None
+    when there is none or the decode sources changed since it was taken."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    blob = text[text.index("```json") + 7:]
+    rec = json.loads(blob[:blob.index("```")])
+    if rec.get("sources_sha256") != decode_sources_sha256():
+        return None
+    return float(rec["hbm_bytes_per_call"])
+
+
+def copy_probe(mib):
+    """A plain device copy of known size (for calibrating the byte counters)."""
+    n = mib * (1 << 20)
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
 
 
 def log(*a):
@@ -259,6 +300,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="headline decode workload only")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain copy of MIB MiB three times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the library has no multi-GPU path "
@@ -266,6 +309,9 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
 
     # ---- headline: soft-capped decode -------------------------------------------------
     head = DecodeBench("softcap_decode_bf16", args.copies, dev)
@@ -301,7 +347,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "attn_decode (decode_stream_kernel + "
                      "decode_merge_kernel)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
+                     "traffic_unit": "HBM bytes per attn_decode call",
                      "call_us": round(a_ms * 1e3, 2), "bytes_per_call": head.bytes,
                      "write_call_us": round(w_ms * 1e3, 2)},
     }
