@@ -61,6 +61,8 @@ PREFILL_CASES = [
     ("bf16", 32, 4, 512, 0, 0.0, True, ([260, 90], [100, 1])),
     ("bf16", 8, 1, 512, 33, 25.0, True, ([140], [140])),
     ("bf16", 4, 2, 128, 16, 10.0, False, ([1, 16, 17, 48], [1, 16, 17, 20])),
+    # a sequence with no new tokens in the middle of the batch: it contributes no rows
+    ("bf16", 8, 4, 256, 24, 0.0, False, ([50, 30, 64], [20, 0, 64])),
     ("fp32", 4, 2, 256, 128, 0.0, False, ([256], [256])),
     ("fp32", 8, 2, 512, 0, 0.0, True, ([90, 31], [30, 31])),
 ]
