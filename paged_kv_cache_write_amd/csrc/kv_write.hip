@@ -1,6 +1,11 @@
-// kv_write.hip -- fused RMSNorm + rotary embedding + paged scatter (one wavefront per row).
+// kv_write.hip -- fused RMSNorm + rotary embedding + paged scatter.
 //
-// One 64-lane wavefront handles one (token, head) row of q, k or v.  With rotate-half RoPE the
+// A workgroup owns one token and a group of its head slots (q heads, then k heads, then v
+// heads).  It first computes the token's rotation table -- cos and sin of t * omega_k for the
+// D/2 frequencies, in double precision -- once into LDS, then each of its 4 wavefronts takes
+// one (token, head) row at a time.  Large batches give a workgroup all slots of its token;
+// small ones (a decode step) split a token's slots over several workgroups so that the launch
+// still fills the chip.  Each wave issues the loads of 4 rows before it processes the first.  With rotate-half RoPE the
 // pair (k, k + D/2) must sit in one lane, so lane l holds the C = D/128 consecutive elements
 // starting at l*C of the first half and the matching C of the second half.  The norm's sum of
 // squares is a wavefront reduction; the norm and the rotation run in double precision and the
@@ -32,6 +37,7 @@ struct KvWriteArgs {
   int64_t num_blocks;
   int32_t max_blocks, batch, total_tokens;
   int32_t Hq, Hkv, nslots, has_q, k_eq_v;
+  int32_t slots_per_wg, groups;  // head slots per workgroup; workgroups per token
   double theta, eps;
 };
 
@@ -39,20 +45,48 @@ template <typename T>
 struct Elem;
 template <>
 struct Elem<float> {
-  static __device__ __forceinline__ double load(const void* p, int64_t i) {
-    return (double)((const float*)p)[i];
-  }
+  static __device__ __forceinline__ double widen(float x) { return (double)x; }
   static __device__ __forceinline__ void store(void* p, int64_t i, double x) {
     ((float*)p)[i] = (float)x;  // round to nearest even
   }
 };
 template <>
 struct Elem<uint16_t> {
-  static __device__ __forceinline__ double load(const void* p, int64_t i) {
-    return (double)bf16_to_f32(((const uint16_t*)p)[i]);
-  }
+  static __device__ __forceinline__ double widen(uint16_t x) { return (double)bf16_to_f32(x); }
   static __device__ __forceinline__ void store(void* p, int64_t i, double x) {
     ((uint16_t*)p)[i] = f64_to_bf16(x);
+  }
+};
+
+constexpr int kRowsInFlight = 4;  // (token, head) rows whose loads one wave keeps in flight
+
+// One (token, head) row of q, k or v as this lane sees it: C elements of each half.
+template <typename T, int C>
+struct Row {
+  bool valid;
+  int kind, h;  // kind 0 = q, 1 = k, 2 = v
+  const T* src;
+  const float* w;
+  int64_t base;
+  T v1[C], v2[C];
+  __device__ __forceinline__ void locate(const KvWriteArgs& a, int slot, int64_t tok, int D) {
+    if (a.has_q && slot < a.Hq) { kind = 0; h = slot; }
+    else {
+      const int s = slot - (a.has_q ? a.Hq : 0);
+      if (s < a.Hkv) { kind = 1; h = s; } else { kind = 2; h = s - a.Hkv; }
+    }
+    src = (const T*)(kind == 0 ? (const void*)a.q : kind == 1 ? a.k : a.v);
+    w = kind == 0 ? a.wq : kind == 1 ? a.wk : a.wv;
+    const int heads = kind == 0 ? a.Hq : a.Hkv;
+    base = (tok * heads + h) * (int64_t)D;
+  }
+  template <int H>
+  __device__ __forceinline__ void load(int lane) {
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      v1[i] = src[base + lane * C + i];
+      v2[i] = src[base + H + lane * C + i];
+    }
   }
 };
 
@@ -60,98 +94,127 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
   constexpr int C = D / 128;  // elements per lane in each half
   constexpr int H = D / 2;
-  const int lane = threadIdx.x & 63;
-  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t tok = wid / a.nslots;
-  const int slot = (int)(wid - tok * a.nslots);
+  __shared__ double cos_t[H], sin_t[H];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t tok = blockIdx.x / a.groups;
+  const int group = (int)(blockIdx.x - tok * a.groups);
   if (tok >= a.total_tokens) return;
 
-  // sequence that owns this token: the last b with cu[b] <= tok
-  int lo = 0, hi = a.batch;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.cu[mid] <= tok) lo = mid; else hi = mid;
-  }
-  const int b = lo;
+  // sequence that owns this token: the b with cu[b] <= tok < cu[b + 1] (one parallel probe
+  // per sequence instead of a chain of dependent loads; empty sequences never match)
+  __shared__ int owner;
+  if (threadIdx.x == 0) owner = -1;
+  __syncthreads();
+  for (int i = threadIdx.x; i < a.batch; i += 256)
+    if (a.cu[i] <= tok && tok < a.cu[i + 1]) owner = i;
+  __syncthreads();
+  const int b = owner;
+  if (b < 0) return;  // tok beyond cu[batch]: nothing owns it
   const int64_t n = (int64_t)a.cu[b + 1] - a.cu[b];
   const int64_t t = (int64_t)a.ctx[b] - n + (tok - a.cu[b]);
   const int64_t page = t >> 4;
   if (t < 0 || page >= a.max_blocks) return;  // inconsistent metadata: write nothing
   const int64_t blk = a.bt[(int64_t)b * a.max_blocks + page];
-  if (blk < 0 || blk >= a.num_blocks) return;
+  if (blk < 0 || blk >= a.num_blocks) return;  // (all three exits are workgroup-uniform)
   const int64_t off = t & 15;
 
-  // which tensor and head this wavefront owns
-  int kind, h;  // kind 0 = q, 1 = k, 2 = v
-  if (a.has_q && slot < a.Hq) { kind = 0; h = slot; }
-  else {
-    const int s = slot - (a.has_q ? a.Hq : 0);
-    if (s < a.Hkv) { kind = 1; h = s; } else { kind = 2; h = s - a.Hkv; }
-  }
-  const void* src = kind == 0 ? (const void*)a.q : kind == 1 ? a.k : a.v;
-  const float* w = kind == 0 ? a.wq : kind == 1 ? a.wk : a.wv;
-  const int heads = kind == 0 ? a.Hq : a.Hkv;
-  const int64_t base = (tok * heads + h) * (int64_t)D;
-
-  double x1[C], x2[C];
-#pragma unroll
-  for (int i = 0; i < C; ++i) {
-    x1[i] = Elem<T>::load(src, base + lane * C + i);
-    x2[i] = Elem<T>::load(src, base + H + lane * C + i);
-  }
-  if (w) {
-    double ss = 0.0;
-#pragma unroll
-    for (int i = 0; i < C; ++i) ss += x1[i] * x1[i] + x2[i] * x2[i];
-    ss = wave_sum_f64(ss);
-    const double inv = 1.0 / sqrt(ss / D + a.eps);
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-      x1[i] = x1[i] * inv * (double)w[lane * C + i];
-      x2[i] = x2[i] * inv * (double)w[H + lane * C + i];
-    }
-  }
-  if (kind != 2 && a.theta > 0.0) {
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-      const int kk = lane * C + i;
-      const double omega = 1.0 / pow(a.theta, (2.0 * kk) / (double)D);
+  // rotation table of position t: omega_k = theta^(-2k/D), angle t * omega_k
+  const bool rope = a.theta > 0.0;
+  if (rope) {
+    for (int k = threadIdx.x; k < H; k += 256) {
+      const double omega = 1.0 / pow(a.theta, (2.0 * k) / (double)D);
       double sn, cs;
       sincos((double)t * omega, &sn, &cs);
-      const double y1 = x1[i] * cs - x2[i] * sn;
-      const double y2 = x2[i] * cs + x1[i] * sn;
-      x1[i] = y1;
-      x2[i] = y2;
+      cos_t[k] = cs;
+      sin_t[k] = sn;
     }
   }
-  if (kind == 0) {
+  __syncthreads();
+
+  const int s0 = group * a.slots_per_wg;
+  const int s1 = s0 + a.slots_per_wg < a.nslots ? s0 + a.slots_per_wg : a.nslots;
+  // the rows of this wave, kRowsInFlight at a time: all their loads are issued before the
+  // first row is processed
+  constexpr int U = kRowsInFlight;
+  for (int first = s0 + wave; first < s1; first += 4 * U) {
+    Row<T, C> rows[U];
 #pragma unroll
-    for (int i = 0; i < C; ++i) {
-      Elem<T>::store(a.q, base + lane * C + i, x1[i]);
-      Elem<T>::store(a.q, base + H + lane * C + i, x2[i]);
+    for (int u = 0; u < U; ++u) {
+      const int slot = first + 4 * u;
+      rows[u].valid = slot < s1;
+      if (rows[u].valid) rows[u].locate(a, slot, tok, D);
+      if (rows[u].valid) rows[u].template load<H>(lane);
     }
-  } else if (kind == 1) {
-    const int64_t row = ((blk * a.Hkv + h) * kPage + off) * D;
 #pragma unroll
-    for (int i = 0; i < C; ++i) {
-      Elem<T>::store(a.kc, row + lane * C + i, x1[i]);
-      Elem<T>::store(a.kc, row + H + lane * C + i, x2[i]);
-    }
-  } else {
-    const int64_t pg = (blk * a.Hkv + h) * (int64_t)D * kPage;
+    for (int u = 0; u < U; ++u) {
+      if (!rows[u].valid) continue;
+      const Row<T, C>& r = rows[u];
+      double x1[C], x2[C];
 #pragma unroll
-    for (int i = 0; i < C; ++i) {
-      Elem<T>::store(a.vc, pg + (int64_t)(lane * C + i) * kPage + off, x1[i]);
-      Elem<T>::store(a.vc, pg + (int64_t)(H + lane * C + i) * kPage + off, x2[i]);
+      for (int i = 0; i < C; ++i) {
+        x1[i] = Elem<T>::widen(r.v1[i]);
+        x2[i] = Elem<T>::widen(r.v2[i]);
+      }
+      if (r.w) {
+        double ss = 0.0;
+#pragma unroll
+        for (int i = 0; i < C; ++i) ss += x1[i] * x1[i] + x2[i] * x2[i];
+        ss = wave_sum_f64(ss);
+        const double inv = 1.0 / sqrt(ss / D + a.eps);
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+          x1[i] = x1[i] * inv * (double)r.w[lane * C + i];
+          x2[i] = x2[i] * inv * (double)r.w[H + lane * C + i];
+        }
+      }
+      if (r.kind != 2 && rope) {
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+          const double cs = cos_t[lane * C + i], sn = sin_t[lane * C + i];
+          const double y1 = x1[i] * cs - x2[i] * sn;
+          const double y2 = x2[i] * cs + x1[i] * sn;
+          x1[i] = y1;
+          x2[i] = y2;
+        }
+      }
+      if (r.kind == 0) {
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+          Elem<T>::store(a.q, r.base + lane * C + i, x1[i]);
+          Elem<T>::store(a.q, r.base + H + lane * C + i, x2[i]);
+        }
+      } else if (r.kind == 1) {
+        const int64_t row = ((blk * a.Hkv + r.h) * kPage + off) * D;
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+          Elem<T>::store(a.kc, row + lane * C + i, x1[i]);
+          Elem<T>::store(a.kc, row + H + lane * C + i, x2[i]);
+        }
+      } else {
+        const int64_t pg = (blk * a.Hkv + r.h) * (int64_t)D * kPage;
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+          Elem<T>::store(a.vc, pg + (int64_t)(lane * C + i) * kPage + off, x1[i]);
+          Elem<T>::store(a.vc, pg + (int64_t)(H + lane * C + i) * kPage + off, x2[i]);
+        }
+      }
     }
   }
 }
 
 template <typename T, int D>
-hipError_t launch_t(const KvWriteArgs& a, hipStream_t s) {
-  const int64_t waves = (int64_t)a.total_tokens * a.nslots;
-  const int64_t blocks = (waves + 3) / 4;
-  if (blocks == 0) return hipSuccess;
+hipError_t launch_t(KvWriteArgs a, hipStream_t s) {
+  if (a.total_tokens == 0 || a.nslots == 0) return hipSuccess;
+  // Slots per workgroup: all of a token's when there are enough tokens to fill the chip
+  // (about 2048 workgroups of 4 waves), otherwise down to one slot per wave.
+  const int64_t rows = (int64_t)a.total_tokens * a.nslots;
+  int64_t per_wave = (rows + 4 * 2048 - 1) / (4 * 2048);
+  const int64_t max_per_wave = (a.nslots + 3) / 4;
+  per_wave = per_wave < 1 ? 1 : (per_wave > max_per_wave ? max_per_wave : per_wave);
+  a.slots_per_wg = (int)(4 * per_wave);
+  a.groups = (a.nslots + a.slots_per_wg - 1) / a.slots_per_wg;
+  const int64_t blocks = (int64_t)a.total_tokens * a.groups;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((kv_write_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
