@@ -13,11 +13,16 @@
 // GQA group share every key tile.  Each wave holds 32 rows (two 16-column MFMA blocks; 16 rows
 // at head size 512) with Q^T and the O^T accumulators in registers.  Key tiles of 32 keys (two
 // pages) are copied from HBM straight into LDS by global_load_lds_dwordx4 (no registers
-// involved) through a ring of up to 4 stages of K and V^T tiles; one barrier per tile both
-// publishes a tile and frees a stage.  Only tiles that intersect the band
-// [past + i - W + 1, past + i] of some row are visited; tiles whose every key is visible to
-// every row of a wave skip all masking.  Keys past the context (only in the last tile) are
-// zeroed in LDS once, so no value read needs a mask.
+// involved) through rings of K and V^T tiles (4 stages each, 2 at head size 512); one barrier
+// per tile both publishes a tile and frees a stage.  A wave's copies for a later tile are
+// spread over the matrix-core instructions of the current one (K copies among the QK^T
+// products, V copies among the P.V products) instead of queueing behind the barrier.  Block
+// ids come through the scalar cache, one load per tile, fetched at the end of the previous
+// iteration.  Only tiles that intersect the band [past + i - W + 1, past + i] of some row of
+// the workgroup are visited, and every wave runs all of them (a tile outside a wave's rows is
+// masked whole); tiles whose every key is visible to every row of a wave skip all masking.
+// Keys past the context (only in the last tile) are zeroed in LDS once, so no value read
+// needs a mask.
 //
 // Key order inside a tile.  The 16 rows of the first QK^T product of a tile are keys
 // {0-3, 8-11} of each of its two pages and the second product's rows are keys {4-7, 12-15},
@@ -31,8 +36,9 @@
 //   K page  chunk-major: the 16-byte chunk x (elements 8x .. 8x+7) of key row r of page p is
 //           stored at byte 256 x + 16 ((r + 4p) mod 16), so a QK^T fragment read by 16 lanes
 //           (16 distinct rows, one chunk) covers 16 distinct bank groups.
-//   V^T page [D rows][16 keys] (32 bytes a row): the two 16-byte halves of row d are swapped
-//           when bit 3 of d is set.
+//   V^T page [D rows][16 keys] (32 bytes a row), rows in order: the 16 lanes of a lane group
+//           read 16 consecutive rows, one half each (measured conflict-free; swapping the halves
+//           of every other group of 8 rows makes the read 2-way conflicted).
 // Block ids of the workgroup's pages are staged in LDS once per pass, so the loop issues no
 // vector-memory operation except the tile copies, whose completion it counts exactly.
 //
@@ -46,7 +52,6 @@ namespace {
 
 constexpr int kTileKeys = 2 * kPage;  // 32 keys per tile: P.V runs on 16x16x32 MFMAs
 constexpr int kWaves = 8;             // two waves per SIMD, 256 registers each
-constexpr int kMaxIds = 1024;         // block ids staged per pass (512 tiles, 16384 keys)
 
 // MFMA column blocks per wave: 2 (32 rows) up to head size 256, 1 (16 rows) at 512, where
 // 32 rows of Q^T (128 registers) plus O^T (256) would not fit a wave's 256 registers.
@@ -57,21 +62,28 @@ struct Rows {
   static constexpr int kPerWg = kWaves * kPerWave;
 };
 
-// LDS: a ring of K tiles and a ring of V^T tiles (K=V: the K ring only), then the block ids.
+// LDS: a ring of SK K tiles and a ring of SV V^T tiles (K=V: the K ring only) in 128 KiB
+// (measured: a 160 KiB allocation with a deeper K ring at head size 512 runs slower).
+// Iteration it reads K(it) and V(it).
 template <int D, bool KEQV>
 struct TileLds {
   static constexpr int kPageBytes = kPage * D * 2;  // one page of K (or V^T)
   static constexpr int kTile = 2 * kPageBytes;      // one 32-key tile of K (or of V^T)
   static constexpr int kBudget = 128 * 1024;
-  static constexpr int kPerStage = KEQV ? kTile : 2 * kTile;
-  static constexpr int kStages = kBudget / kPerStage >= 4 ? 4 : kBudget / kPerStage;
+  static constexpr int kMaxStages = 4;
+  static constexpr int kFit = kBudget / kTile;      // tiles that fit
+  static constexpr int SK = KEQV ? (kFit < kMaxStages ? kFit : kMaxStages)
+                                 : (kFit >= 2 * kMaxStages ? kMaxStages : (kFit + 1) / 2);
+  static constexpr int SV = KEQV ? 0 : (kFit >= 2 * kMaxStages ? kMaxStages : kFit / 2);
   static constexpr int kKRing = 0;
-  static constexpr int kVRing = kStages * kTile;
-  static constexpr int kIds = kStages * kPerStage;
-  static constexpr int kBytes = kIds + kMaxIds * 4;
+  static constexpr int kVRing = SK * kTile;
+  static constexpr int kBytes = (SK + SV) * kTile;
   static constexpr int kChunks = kTile / 1024;          // 1 KiB copies per tile
   static constexpr int kPerWave = kChunks / kWaves;     // copies per wave per tile
   static_assert(kChunks % kWaves == 0, "tile copies split evenly over the waves");
+  static_assert(SK >= 2 && SK <= kMaxStages && (KEQV ? SK >= 3 : (SV >= 2 && SV <= SK)),
+                "ring depths");
+  static_assert(kBytes <= kBudget, "LDS budget");
 };
 
 // Row of page c16 / 8 that QK^T product m (0, 1) places at MFMA row c16: keys {0-3, 8-11} of
@@ -83,12 +95,28 @@ __device__ __forceinline__ int qk_row_key(int c16, int m) {
 // One HBM -> LDS copy of 1 KiB: each lane moves 16 bytes to M0 + 16 * lane.  Issued through
 // inline assembly so that the compiler does not add waits of its own for the LDS it writes:
 // the kernel waits on the vector-memory counter explicitly before the barrier that
-// publishes a tile.
+// publishes a tile.  No memory clobber: a copy only ever writes a ring stage that no LDS
+// access of the same iteration touches, and being volatile it stays ordered with the
+// barriers and explicit waits that separate iterations.
 __device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds_off) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(src), "s"(lds_off)
-               : "memory", "m0");
+               : "m0");
+}
+
+// Two consecutive int32 (wave-uniform address) through the scalar cache, waited for inside the
+// same statement so the value is complete when the statement ends.  Used only where no LDS
+// read of this wave is outstanding (the wait covers those too).
+__device__ __forceinline__ int2 scalar_load2(const int32_t* p) {
+  int2 v;
+  asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
+  return v;
+}
+__device__ __forceinline__ int scalar_load1(const int32_t* p) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
+  return v;
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding.
@@ -98,28 +126,27 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Copies of one tile of K (V=false) or of V^T (V=true) into `lds_off`.
+// Copy i (0 .. kPerWave-1) of this wave for one tile of K (V=false) or of V^T (V=true) into
+// `lds_off`: 1 KiB chunk wave + kWaves * i of the tile.
 template <int D, bool KEQV, bool V>
-__device__ __forceinline__ void issue_tile(const AttnArgs& a, uint32_t lds_off, int g,
-                                           int64_t blkA, int64_t blkB, int wave, int lane) {
+__device__ __forceinline__ void issue_chunk(const AttnArgs& a, uint32_t lds_off, int g,
+                                            int64_t blkA, int64_t blkB, int wave, int lane,
+                                            int i) {
   using T = TileLds<D, KEQV>;
   constexpr int kChunksPerPage = T::kPageBytes / 1024;
-#pragma unroll
-  for (int i = 0; i < T::kPerWave; ++i) {
-    const int q = wave + kWaves * i;  // 1 KiB chunk of the tile
-    const int page = q / kChunksPerPage, qq = q - page * kChunksPerPage;
-    const int s = qq * 64 + lane;     // 16-byte slot inside the page
-    const int64_t blk = page ? blkB : blkA;
-    const void* src;
-    if constexpr (!V) {
-      const int x = s >> 4, r = ((s & 15) - 4 * page) & 15;  // chunk-major, rotated by 4 page
-      src = a.kc + ((blk * a.Hkv + g) * kPage + r) * D + x * 8;
-    } else {
-      const int d = s >> 1, h = (s & 1) ^ ((d >> 3) & 1);
-      src = a.vc + ((blk * a.Hkv + g) * D + d) * kPage + h * 8;
-    }
-    lds_copy16(src, __builtin_amdgcn_readfirstlane(lds_off + q * 1024));
+  const int q = wave + kWaves * i;  // 1 KiB chunk of the tile
+  const int page = q / kChunksPerPage, qq = q - page * kChunksPerPage;
+  const int s = qq * 64 + lane;     // 16-byte slot inside the page
+  const int64_t blk = page ? blkB : blkA;
+  const void* src;
+  if constexpr (!V) {
+    const int x = s >> 4, r = ((s & 15) - 4 * page) & 15;  // chunk-major, rotated by 4 page
+    src = a.kc + ((blk * a.Hkv + g) * kPage + r) * D + x * 8;
+  } else {
+    const int d = s >> 1, h = s & 1;
+    src = a.vc + ((blk * a.Hkv + g) * D + d) * kPage + h * 8;
   }
+  lds_copy16(src, __builtin_amdgcn_readfirstlane(lds_off + q * 1024));
 }
 
 // Zero, in one staged tile, the values of key slots nvalid .. 31 (keys past the context):
@@ -135,7 +162,7 @@ __device__ __forceinline__ void zero_tail_values(unsigned char* tile, int nvalid
 #pragma unroll
       for (int r = 0; r < kPage; ++r)
         if (page * kPage + r >= nvalid)
-          *(uint16_t*)(row + 16 * ((r >> 3) ^ ((d >> 3) & 1)) + 2 * (r & 7)) = 0;
+          *(uint16_t*)(row + 2 * r) = 0;
     }
   } else {
     // chunk-major K page: 16-byte unit (row r, chunk x) at 256 x + 16 ((r + 4 page) mod 16)
@@ -153,13 +180,11 @@ template <int D, bool CAP, bool KEQV>
 __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs a, int tiles_per_bg,
                                                                      int n_tiles) {
   using T = TileLds<D, KEQV>;
-  constexpr int NC = D / 32, ND = D / 16, R = Rows<D>::kR, S = T::kStages;
+  constexpr int NC = D / 32, ND = D / 16, R = Rows<D>::kR, SK = T::SK, SV = T::SV;
   constexpr int kRowsPerWave = Rows<D>::kPerWave, kRowsPerWg = Rows<D>::kPerWg;
-  static_assert(S >= 2 && S <= 4, "ring depth");
   extern __shared__ __align__(16) unsigned char smem[];
   const uint32_t smem_off =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
-  int* ids = (int*)(smem + T::kIds);
   const int lane = threadIdx.x & 63, c16 = lane & 15, j = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -211,12 +236,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
     span_c[rb] = ok_c[rb] ? (uint32_t)(t - lo) : 0u;
     load_q<D>(qf[rb], a.q + ((int64_t)(q0 + i) * a.Hq + g * G + hh) * D, ok_c[rb]);
   }
-  // wave-uniform bounds: union [vlo, vhi] and intersection [lo_max, hi_min] of the rows' ranges
+  // Complete the Q loads here: left to the compiler, their wait would sit at the first use,
+  // inside the tile loop, and drain the in-flight tile copies on every iteration.
+  wait_vmcnt<0>();
+  // wave-uniform bounds: intersection [lo_max, hi_min] of the rows' key ranges (tiles inside it
+  // need no mask)
   const bool wave_active = wrows > 0;
   const int t_first_w = past + (wave_active ? wrow0 : row0) / G;
   const int t_last_w = past + (wave_active ? wrow0 + wrows - 1 : row0) / G;
-  const int vlo = W > 0 ? (t_first_w - W + 1 > 0 ? t_first_w - W + 1 : 0) : 0;
-  const int vhi = t_last_w;
   const int lo_max = W > 0 ? (t_last_w - W + 1 > 0 ? t_last_w - W + 1 : 0) : 0;
   const int hi_min = t_first_w;
 
@@ -241,164 +268,192 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
 #pragma unroll
   for (int m = 0; m < 2; ++m)
     koff[m] = kpage * T::kPageBytes + 256 * j + 16 * ((qk_row_key(c16, m) + 4 * kpage) & 15);
-  const int voff = (j >> 1) * T::kPageBytes + c16 * 32 + (((j & 1) ^ ((c16 >> 3) & 1)) * 16);
+  const int voff = (j >> 1) * T::kPageBytes + c16 * 32 + (j & 1) * 16;
   // key of score slot e (product e / 4, register e % 4) of this lane group, minus k0
   const int kslot = (j >> 1) * kPage + 8 * (j & 1);
 
-  constexpr int kPerIt = T::kPerWave * (KEQV ? 1 : 2);
-  for (int pass0 = 0; pass0 < ntiles; pass0 += kMaxIds / 2) {
-    const int np = (ntiles - pass0) < kMaxIds / 2 ? (ntiles - pass0) : kMaxIds / 2;
-    // ---- block ids of this pass's pages, staged once (nothing else is in flight here)
-    __syncthreads();  // the previous pass is done with the id table
-    for (int i = threadIdx.x; i < 2 * np; i += 64 * kWaves) {
-      const int page = 2 * (kt0 + pass0) + i;
-      ids[i] = page <= last_page ? (int)clamp_blk(a.bt[bt_row + page], a.num_blocks) : -1;
+  // ---- copy schedule.  Group g (iteration g, or the prologue for g < 0) copies tile
+  // g - 1 + S into the stages that iteration g - 1 has just released; iteration it reads
+  // tile it.
+  const int np = ntiles;
+  // Block ids of a tile's two pages (wave-uniform, through the scalar cache).
+  struct TileIds { int64_t a, b; };
+  auto ids_of = [&](int tile) -> TileIds {
+    TileIds r{0, 0};
+    if (tile < 0 || tile >= ntiles) return r;
+    const int page = 2 * (kt0 + tile);  // <= last_page for every tile of the range
+    if (page + 1 <= last_page) {
+      const int2 v = scalar_load2(a.bt + bt_row + page);
+      r.a = clamp_blk(v.x, a.num_blocks);
+      r.b = clamp_blk(v.y, a.num_blocks);
+    } else {
+      // the second page lies past the context: alias the first (its keys are masked and its
+      // values zeroed) and read nothing past the sequence's last page
+      r.a = r.b = clamp_blk(scalar_load1(a.bt + bt_row + page), a.num_blocks);
     }
-    wait_vmcnt<0>();
+    return r;
+  };
+  // Group grp copies K(grp - 1 + S) and V(grp - 1 + S) (both rings have S stages), the K
+  // copies first.  Every group issues the same number of copies -- past the last tile it
+  // copies block 0 into a stage no iteration reads any more -- so the count of copies that
+  // may stay in flight at a wait is a constant, and no branch sits between the matrix-core
+  // instructions the copies are spread over.
+  static_assert(KEQV || SK == SV, "both rings have the same depth");
+  constexpr int S = SK;
+  constexpr int kPerGroup = T::kPerWave * (KEQV ? 1 : 2);
+  struct Group { uint32_t kdst, vdst; TileIds ids; };
+  auto group_of = [&](int grp) -> Group {
+    const int t = grp - 1 + S;
+    return Group{smem_off + T::kKRing + (t % S) * T::kTile,
+                 smem_off + T::kVRing + (KEQV ? 0 : (t % S) * T::kTile), ids_of(t)};
+  };
+  auto k_chunk = [&](const Group& gr, int i) {
+    issue_chunk<D, KEQV, false>(a, gr.kdst, g, gr.ids.a, gr.ids.b, wave, lane, i);
+  };
+  auto v_chunk = [&](const Group& gr, int i) {
+    if constexpr (!KEQV)
+      issue_chunk<D, KEQV, true>(a, gr.vdst, g, gr.ids.a, gr.ids.b, wave, lane, i);
+  };
+  auto issue_group = [&](const Group& gr) {
+#pragma unroll
+    for (int i = 0; i < T::kPerWave; ++i) k_chunk(gr, i);
+#pragma unroll
+    for (int i = 0; i < T::kPerWave; ++i) v_chunk(gr, i);
+  };
+
+  // prologue: groups 1 - S .. -1 (tiles 0 .. S - 2)
+  for (int grp = 1 - S; grp < 0; ++grp) issue_group(group_of(grp));
+  Group gr = group_of(0);
+
+  for (int it = 0; it < np; ++it) {
+    // tile it (group it + 1 - S) has landed once at most the S - 2 later groups are in flight
+    wait_vmcnt<(S - 2) * kPerGroup>();
     __syncthreads();
-    auto issue = [&](int it) {
-      const int iA = ids[2 * it], iB = ids[2 * it + 1];
-      const int64_t bA = iA, bB = iB >= 0 ? iB : iA;  // past the last page: alias the first
-      issue_tile<D, KEQV, false>(a, smem_off + T::kKRing + (it % S) * T::kTile, g, bA, bB,
-                                 wave, lane);
-      if constexpr (!KEQV)
-        issue_tile<D, KEQV, true>(a, smem_off + T::kVRing + (it % S) * T::kTile, g, bA, bB,
-                                  wave, lane);
-    };
 
-    // Prologue: tiles 0..S-2.  Iteration it consumes tile it and, after the barrier that
-    // proves every wave has left iteration it-1, refills that iteration's stage with tile
-    // it+S-1.
-    for (int u = 0; u < S - 1; ++u)
-      if (u < np) issue(u);
+    const int k0 = (kt0 + it) * kTileKeys;
+    if (k0 + kTileKeys > L) {
+      // Last tile: slots of keys >= L may hold anything, NaN included, and a zero weight
+      // does not cancel a NaN value.  Zero the values of those keys once, in LDS.
+      zero_tail_values<D, KEQV>(smem + (KEQV ? T::kKRing + (it % SK) * T::kTile
+                                             : T::kVRing + (it % SV) * T::kTile),
+                                L - k0);
+      __syncthreads();
+    }
+    // Every wave runs every tile of the workgroup's range: a tile outside a wave's band is
+    // masked whole (its weights are exactly 0) and costs a little matrix-core time, where a
+    // branch around the work would split the copy schedule spread over it.
+    {
+    const unsigned char* kt = smem + T::kKRing + (it % SK) * T::kTile;
 
-    for (int it = 0; it < np; ++it) {
-      // Tile it must have landed.  In steady state the copies issued after it are those of
-      // the last S-2 iterations; once the issues stop (tail) everything is waited for.
-      {
-        const bool tail = it + S - 1 > np;
-        const int after = tail ? 0 : (it < S - 2 ? it : S - 2);
-        if (after >= 2) wait_vmcnt<2 * kPerIt>();
-        else if (after == 1) wait_vmcnt<kPerIt>();
-        else wait_vmcnt<0>();
-        __syncthreads();
-      }
-      if (it + S - 1 < np) issue(it + S - 1);
-
-      const int k0 = (kt0 + pass0 + it) * kTileKeys;
-      if (k0 + kTileKeys > L) {
-        // Last tile: slots of keys >= L may hold anything, NaN included, and a zero weight
-        // does not cancel a NaN value.  Zero the values of those keys once, in LDS.
-        zero_tail_values<D, KEQV>(smem + (it % S) * (KEQV ? T::kTile : 0) +
-                                      (KEQV ? T::kKRing : T::kVRing + (it % S) * T::kTile),
-                                  L - k0);
-        __syncthreads();
-      }
-      if (!wave_active || k0 > vhi || k0 + kTileKeys - 1 < vlo) continue;  // wave-uniform
-      const unsigned char* kt = smem + T::kKRing + (it % S) * T::kTile;
-
-      // ---- S^T = K Q^T: s[m][rb], product m covering the key rows described above
-      float4_t s[2][R];
+    // ---- S^T = K Q^T: s[m][rb], product m covering the key rows described above
+    float4_t s[2][R];
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int rb = 0; rb < R; ++rb) s[m][rb] = float4_t{0.f, 0.f, 0.f, 0.f};
+      for (int rb = 0; rb < R; ++rb) s[m][rb] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
+    for (int c = 0; c < NC; ++c) {
+      if (c % (NC / T::kPerWave) == 0) k_chunk(gr, c / (NC / T::kPerWave));
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const bf16x8_t kf = as_bf16x8(*(const u32x4_t*)(kt + koff[m] + 1024 * c));
+      for (int m = 0; m < 2; ++m) {
+        const bf16x8_t kf = as_bf16x8(*(const u32x4_t*)(kt + koff[m] + 1024 * c));
 #pragma unroll
-          for (int rb = 0; rb < R; ++rb) s[m][rb] = mfma_16x16x32(kf, qf[rb][c], s[m][rb]);
-        }
-
-      // ---- scores on the log2 scale, band + causal mask (skipped when the whole tile is
-      // visible to every row of the wave)
-      const bool full = k0 >= lo_max && k0 + kTileKeys - 1 <= hi_min;
-      float xs[R][8];
-#pragma unroll
-      for (int rb = 0; rb < R; ++rb)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) xs[rb][e] = to_log2<CAP>(s[e >> 2][rb][e & 3], a.sc);
-      if (!full) {
-        const int kk = k0 + kslot;
-#pragma unroll
-        for (int rb = 0; rb < R; ++rb) {
-          const int d0 = kk - lo_c[rb];
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            xs[rb][e] = (uint32_t)(d0 + e) <= span_c[rb] ? xs[rb][e] : -INFINITY;
-        }
-      }
-      // ---- online softmax with a lazily moved reference: the reference moves only when a
-      // weight would exceed 2^8, so most tiles skip the rescale of O
-      bool need = false;
-      float mx[R];
-#pragma unroll
-      for (int rb = 0; rb < R; ++rb) {
-        float m = fmaxf(fmaxf(fmaxf(xs[rb][0], xs[rb][1]), fmaxf(xs[rb][2], xs[rb][3])),
-                        fmaxf(fmaxf(xs[rb][4], xs[rb][5]), fmaxf(xs[rb][6], xs[rb][7])));
-        m = max_over_groups(m);
-        mx[rb] = m;
-        need |= m > m_ref[rb] + 8.0f;
-      }
-      if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-        for (int rb = 0; rb < R; ++rb) {
-          const float m_new = mx[rb] > m_ref[rb] + 8.0f ? mx[rb] : m_ref[rb];
-          const float alpha = m_ref[rb] == -INFINITY ? 1.f : fast_exp2(m_ref[rb] - m_new);
-          l_run[rb] *= alpha;
-#pragma unroll
-          for (int nn = 0; nn < ND; ++nn) o[rb][nn] *= alpha;
-          m_ref[rb] = m_new;
-        }
-      }
-      bf16x8_t pf[R];
-#pragma unroll
-      for (int rb = 0; rb < R; ++rb) {
-        const float mu = m_ref[rb] == -INFINITY ? 0.f : m_ref[rb];
-        bf16x2_t pw[4];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          pw[w] = cvt_bf16x2(fast_exp2(xs[rb][2 * w] - mu), fast_exp2(xs[rb][2 * w + 1] - mu));
-          // the row sum uses the same bf16-rounded weights that multiply V
-          l_run[rb] = sum_bf16x2(pw[w], l_run[rb]);
-        }
-        pf[rb] = bf16x8_t{pw[0][0], pw[0][1], pw[1][0], pw[1][1],
-                          pw[2][0], pw[2][1], pw[3][0], pw[3][1]};
-      }
-
-      // ---- O^T[d][row] += V^T[d][keys] P^T[keys][row]
-      if constexpr (!KEQV) {
-        const unsigned char* vp = smem + T::kVRing + (it % S) * T::kTile + voff;
-#pragma unroll
-        for (int nn = 0; nn < ND; ++nn) {
-          const bf16x8_t af = as_bf16x8(*(const u32x4_t*)(vp + nn * 512));
-#pragma unroll
-          for (int rb = 0; rb < R; ++rb) o[rb][nn] = mfma_16x16x32(af, pf[rb], o[rb][nn]);
-        }
-      } else {
-        // values are the keys: gather K[key][d] column-wise from the chunk-major K page;
-        // key 8 (j % 2) + e of page j / 2 at d = 16 nn + c16
-        const int pg = j >> 1;
-        const int kb = pg * T::kPageBytes + 256 * (c16 >> 3) + 2 * (c16 & 7);
-        const int rot = 8 * (j & 1) + 4 * pg;
-#pragma unroll
-        for (int nn = 0; nn < ND; ++nn) {
-          uint32_t w[4];
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            const unsigned char* p0 = kt + kb + 512 * nn + 16 * ((rot + 2 * e2) & 15);
-            const unsigned char* p1 = kt + kb + 512 * nn + 16 * ((rot + 2 * e2 + 1) & 15);
-            w[e2] = (uint32_t)(*(const uint16_t*)p0) | ((uint32_t)(*(const uint16_t*)p1) << 16);
-          }
-          const bf16x8_t af = as_bf16x8(u32x4_t{w[0], w[1], w[2], w[3]});
-#pragma unroll
-          for (int rb = 0; rb < R; ++rb) o[rb][nn] = mfma_16x16x32(af, pf[rb], o[rb][nn]);
-        }
+        for (int rb = 0; rb < R; ++rb) s[m][rb] = mfma_16x16x32(kf, qf[rb][c], s[m][rb]);
       }
     }
+
+    // ---- scores on the log2 scale, band + causal mask (skipped when the whole tile is
+    // visible to every row of the wave)
+    const bool full = k0 >= lo_max && k0 + kTileKeys - 1 <= hi_min;
+    float xs[R][8];
+#pragma unroll
+    for (int rb = 0; rb < R; ++rb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xs[rb][e] = to_log2<CAP>(s[e >> 2][rb][e & 3], a.sc);
+    if (!full) {
+      const int kk = k0 + kslot;
+#pragma unroll
+      for (int rb = 0; rb < R; ++rb) {
+        const int d0 = kk - lo_c[rb];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          xs[rb][e] = (uint32_t)(d0 + e) <= span_c[rb] ? xs[rb][e] : -INFINITY;
+      }
+    }
+    // ---- online softmax with a lazily moved reference: the reference moves only when a
+    // weight would exceed 2^8, so most tiles skip the rescale of O
+    bool need = false;
+    float mx[R];
+#pragma unroll
+    for (int rb = 0; rb < R; ++rb) {
+      float m = fmaxf(fmaxf(fmaxf(xs[rb][0], xs[rb][1]), fmaxf(xs[rb][2], xs[rb][3])),
+                      fmaxf(fmaxf(xs[rb][4], xs[rb][5]), fmaxf(xs[rb][6], xs[rb][7])));
+      m = max_over_groups(m);
+      mx[rb] = m;
+      need |= m > m_ref[rb] + 8.0f;
+    }
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+      for (int rb = 0; rb < R; ++rb) {
+        const float m_new = mx[rb] > m_ref[rb] + 8.0f ? mx[rb] : m_ref[rb];
+        const float alpha = m_ref[rb] == -INFINITY ? 1.f : fast_exp2(m_ref[rb] - m_new);
+        l_run[rb] *= alpha;
+#pragma unroll
+        for (int nn = 0; nn < ND; ++nn) o[rb][nn] *= alpha;
+        m_ref[rb] = m_new;
+      }
+    }
+    bf16x8_t pf[R];
+#pragma unroll
+    for (int rb = 0; rb < R; ++rb) {
+      const float mu = m_ref[rb] == -INFINITY ? 0.f : m_ref[rb];
+      bf16x2_t pw[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        pw[w] = cvt_bf16x2(fast_exp2(xs[rb][2 * w] - mu), fast_exp2(xs[rb][2 * w + 1] - mu));
+        // the row sum uses the same bf16-rounded weights that multiply V
+        l_run[rb] = sum_bf16x2(pw[w], l_run[rb]);
+      }
+      pf[rb] = bf16x8_t{pw[0][0], pw[0][1], pw[1][0], pw[1][1],
+                        pw[2][0], pw[2][1], pw[3][0], pw[3][1]};
+    }
+
+    // ---- O^T[d][row] += V^T[d][keys] P^T[keys][row]
+    if constexpr (!KEQV) {
+      const unsigned char* vp = smem + T::kVRing + (it % SV) * T::kTile + voff;
+#pragma unroll
+      for (int nn = 0; nn < ND; ++nn) {
+        if (nn % (ND / T::kPerWave) == 0) v_chunk(gr, nn / (ND / T::kPerWave));
+        const bf16x8_t af = as_bf16x8(*(const u32x4_t*)(vp + nn * 512));
+#pragma unroll
+        for (int rb = 0; rb < R; ++rb) o[rb][nn] = mfma_16x16x32(af, pf[rb], o[rb][nn]);
+      }
+    } else {
+      // values are the keys: gather K[key][d] column-wise from the chunk-major K page;
+      // key 8 (j % 2) + e of page j / 2 at d = 16 nn + c16
+      const int pg = j >> 1;
+      const int kb = pg * T::kPageBytes + 256 * (c16 >> 3) + 2 * (c16 & 7);
+      const int rot = 8 * (j & 1) + 4 * pg;
+#pragma unroll
+      for (int nn = 0; nn < ND; ++nn) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const unsigned char* p0 = kt + kb + 512 * nn + 16 * ((rot + 2 * e2) & 15);
+          const unsigned char* p1 = kt + kb + 512 * nn + 16 * ((rot + 2 * e2 + 1) & 15);
+          w[e2] = (uint32_t)(*(const uint16_t*)p0) | ((uint32_t)(*(const uint16_t*)p1) << 16);
+        }
+        const bf16x8_t af = as_bf16x8(u32x4_t{w[0], w[1], w[2], w[3]});
+#pragma unroll
+        for (int rb = 0; rb < R; ++rb) o[rb][nn] = mfma_16x16x32(af, pf[rb], o[rb][nn]);
+      }
+    }
+    }
+    // the next group's tile ids, fetched here (not at the barrier, where every wave of the
+    // workgroup would wait for them at the same moment)
+    gr = group_of(it + 1);
   }
+  wait_vmcnt<0>();  // no copy may land in LDS after the workgroup has left it
 
   if (!wave_active) return;
 #pragma unroll
