@@ -151,7 +151,8 @@ def attn_decode(p: LayerParams, q, k_cache, v_cache, block_table, context_lens,
         _ptr(v_cache, "v_cache", et), k_cache.shape[0],
         _ptr(block_table, "block_table", torch.int32), block_table.shape[1],
         _ptr(context_lens, "context_lens", torch.int32), B, int(max_context_len),
-        _ptr(out, "out", et), _ptr(workspace, "workspace"), workspace.numel(), _stream(stream))
+        _ptr(out, "out", et), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
     _raise_on(st)
     return out
 

@@ -39,8 +39,8 @@
 //   V^T page [D rows][16 keys] (32 bytes a row), rows in order: the 16 lanes of a lane group
 //           read 16 consecutive rows, one half each (measured conflict-free; swapping the halves
 //           of every other group of 8 rows makes the read 2-way conflicted).
-// Block ids of the workgroup's pages are staged in LDS once per pass, so the loop issues no
-// vector-memory operation except the tile copies, whose completion it counts exactly.
+// The tile loop issues no vector-memory operation other than the tile copies (the Q loads
+// are complete before it starts), so the copies' completion is counted exactly.
 //
 // Order of work: workgroup ids are dealt to the 8 XCDs round robin, so consecutive logical
 // tiles are given to one XCD (its L2 then serves the key tiles shared by neighbouring row

@@ -188,3 +188,43 @@ def test_k_eq_v_equals_separate_caches_holding_the_same_tensor():
     b = case2.prefill(qd, cu, cl)
     torch.cuda.synchronize()
     assert_same_result(a, b)
+
+
+def test_decode_workspace_reused_across_calls_of_other_shapes():
+    """One workspace, sized once for the largest call, serves consecutive calls of other batch
+    sizes and length mixes: nothing a call leaves in it may leak into the next one."""
+    spec = wl.LayerSpec("bf16", 8, 2, 256, window=0, rope_theta=1e4)
+    p = None
+    ws = None
+    for k, lens in enumerate([[900, 17, 3000, 1], [2500, 640], [5, 4096, 333, 1200, 77]]):
+        pb = wl.paged_batch(lens, [1] * len(lens), seed=60 + k)
+        case = PagedCase(spec, pb, 60 + k)
+        case.write([L - 1 for L in lens], [L - 1 for L in lens], 160 + k, with_q=False)
+        q, kk, v, qd, cu, cl = case.write(lens, [1] * len(lens), 60 + k)
+        if ws is None:
+            p = case.p
+            ws = ga.decode_workspace(p, 8, 4096)
+        out = ga.attn_decode(case.p, qd, case.kc, case.vc, case.bt, i32(cl, "cuda"), max(lens),
+                             workspace=ws)
+        torch.cuda.synchronize()
+        ref = case.oracle_attention(qd, cu, cl)
+        assert_attn_close(out, ref, "bf16", what=f"workspace reuse call {k}")
+
+
+def test_decode_sequence_without_keys_gives_zero_output():
+    """A sequence whose context is empty (length 0) has no keys: its output rows are zero,
+    and the other sequences of the batch are unaffected."""
+    spec = wl.LayerSpec("bf16", 8, 4, 256, window=0, rope_theta=1e4)
+    lens = [300, 1, 45]
+    pb = wl.paged_batch(lens, [1] * 3, seed=64)
+    case = PagedCase(spec, pb, 64)
+    case.write([299, 0, 44], [299, 0, 44], 164, with_q=False)
+    q, k, v, qd, cu, cl = case.write(lens, [1] * 3, 64)
+    cl0 = cl.copy()
+    cl0[1] = 0
+    out = ga.attn_decode(case.p, qd, case.kc, case.vc, case.bt, i32(cl0, "cuda"), 300)
+    torch.cuda.synchronize()
+    assert (out[1].float() == 0).all()
+    ref = case.oracle_attention(qd, cu, cl)
+    keep = [0, 2]
+    assert_attn_close(out[keep], ref[keep], "bf16", what="decode with an empty sequence")
