@@ -293,57 +293,43 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
     }
     return r;
   };
-  // Group grp copies K(grp - 1 + S) and V(grp - 1 + S) (both rings have S stages), the K
-  // copies first.  Every group issues the same number of copies -- past the last tile it
-  // copies block 0 into a stage no iteration reads any more -- so the count of copies that
-  // may stay in flight at a wait is a constant, and no branch sits between the matrix-core
-  // instructions the copies are spread over.
+  // Both rings have S stages.  Iteration jj (one barrier) consumes the TB tiles TB*jj ..
+  // TB*jj + TB - 1 (two when the ring has four stages, one when it has two) and, in the stages
+  // the previous iteration released, copies tiles TB*jj + S - TB .. + TB - 1.  All of those
+  // copies are spread over the work on the iteration's first tile (K copies among the QK^T
+  // products, V copies among the P.V products), so that at least one tile's work hides the
+  // latency of the last of them.  Past the last tile the copies read block 0 into stages no
+  // iteration reads any more, so every iteration issues the same number of copies and the
+  // count of copies that may stay in flight at a wait is a constant (no branch sits between
+  // the matrix-core instructions the copies are spread over).
   static_assert(KEQV || SK == SV, "both rings have the same depth");
   constexpr int S = SK;
-  constexpr int kPerGroup = T::kPerWave * (KEQV ? 1 : 2);
-  struct Group { uint32_t kdst, vdst; TileIds ids; };
-  auto group_of = [&](int grp) -> Group {
-    const int t = grp - 1 + S;
-    return Group{smem_off + T::kKRing + (t % S) * T::kTile,
-                 smem_off + T::kVRing + (KEQV ? 0 : (t % S) * T::kTile), ids_of(t)};
+  constexpr int TB = S >= 4 ? 2 : 1;
+  static_assert(S % TB == 0 && S >= 2 * TB, "ring depth");
+  constexpr int kPerTile = T::kPerWave * (KEQV ? 1 : 2);
+  constexpr int kWait = (S / TB - 2) * TB * kPerTile;  // copies of later iterations in flight
+  auto k_chunk = [&](int t, const TileIds& ids, int i) {
+    issue_chunk<D, KEQV, false>(a, smem_off + T::kKRing + (t % S) * T::kTile, g, ids.a, ids.b,
+                                wave, lane, i);
   };
-  auto k_chunk = [&](const Group& gr, int i) {
-    issue_chunk<D, KEQV, false>(a, gr.kdst, g, gr.ids.a, gr.ids.b, wave, lane, i);
-  };
-  auto v_chunk = [&](const Group& gr, int i) {
+  auto v_chunk = [&](int t, const TileIds& ids, int i) {
     if constexpr (!KEQV)
-      issue_chunk<D, KEQV, true>(a, gr.vdst, g, gr.ids.a, gr.ids.b, wave, lane, i);
+      issue_chunk<D, KEQV, true>(a, smem_off + T::kVRing + (t % S) * T::kTile, g, ids.a,
+                                 ids.b, wave, lane, i);
   };
-  auto issue_group = [&](const Group& gr) {
+  auto issue_tile = [&](int t, const TileIds& ids) {
 #pragma unroll
-    for (int i = 0; i < T::kPerWave; ++i) k_chunk(gr, i);
+    for (int i = 0; i < T::kPerWave; ++i) k_chunk(t, ids, i);
 #pragma unroll
-    for (int i = 0; i < T::kPerWave; ++i) v_chunk(gr, i);
+    for (int i = 0; i < T::kPerWave; ++i) v_chunk(t, ids, i);
   };
 
-  // prologue: groups 1 - S .. -1 (tiles 0 .. S - 2)
-  for (int grp = 1 - S; grp < 0; ++grp) issue_group(group_of(grp));
-  Group gr = group_of(0);
-
-  for (int it = 0; it < np; ++it) {
-    // tile it (group it + 1 - S) has landed once at most the S - 2 later groups are in flight
-    wait_vmcnt<(S - 2) * kPerGroup>();
-    __syncthreads();
-
-    const int k0 = (kt0 + it) * kTileKeys;
-    if (k0 + kTileKeys > L) {
-      // Last tile: slots of keys >= L may hold anything, NaN included, and a zero weight
-      // does not cancel a NaN value.  Zero the values of those keys once, in LDS.
-      zero_tail_values<D, KEQV>(smem + (KEQV ? T::kKRing + (it % SK) * T::kTile
-                                             : T::kVRing + (it % SV) * T::kTile),
-                                L - k0);
-      __syncthreads();
-    }
-    // Every wave runs every tile of the workgroup's range: a tile outside a wave's band is
-    // masked whole (its weights are exactly 0) and costs a little matrix-core time, where a
-    // branch around the work would split the copy schedule spread over it.
-    {
-    const unsigned char* kt = smem + T::kKRing + (it % SK) * T::kTile;
+  // One tile: S^T, mask, online softmax, O^T; on the way it copies the `ncp` (a compile-time
+  // count) tiles ct, ct + 1, .. whose ids are cids[0], cids[1], ..
+  auto process_tile = [&](int t, auto ncp, int ct, const TileIds* cids) {
+    constexpr int Q = decltype(ncp)::value * T::kPerWave;  // copies of each ring
+    const int k0 = (kt0 + t) * kTileKeys;
+    const unsigned char* kt = smem + T::kKRing + (t % S) * T::kTile;
 
     // ---- S^T = K Q^T: s[m][rb], product m covering the key rows described above
     float4_t s[2][R];
@@ -353,7 +339,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
       for (int rb = 0; rb < R; ++rb) s[m][rb] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      if (c % (NC / T::kPerWave) == 0) k_chunk(gr, c / (NC / T::kPerWave));
+#pragma unroll
+      for (int q = c * Q / NC; q < (c + 1) * Q / NC; ++q)
+        k_chunk(ct + q / T::kPerWave, cids[q / T::kPerWave], q % T::kPerWave);
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const bf16x8_t kf = as_bf16x8(*(const u32x4_t*)(kt + koff[m] + 1024 * c));
@@ -420,10 +408,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
 
     // ---- O^T[d][row] += V^T[d][keys] P^T[keys][row]
     if constexpr (!KEQV) {
-      const unsigned char* vp = smem + T::kVRing + (it % SV) * T::kTile + voff;
+      const unsigned char* vp = smem + T::kVRing + (t % S) * T::kTile + voff;
 #pragma unroll
       for (int nn = 0; nn < ND; ++nn) {
-        if (nn % (ND / T::kPerWave) == 0) v_chunk(gr, nn / (ND / T::kPerWave));
+#pragma unroll
+        for (int q = nn * Q / ND; q < (nn + 1) * Q / ND; ++q)
+          v_chunk(ct + q / T::kPerWave, cids[q / T::kPerWave], q % T::kPerWave);
         const bf16x8_t af = as_bf16x8(*(const u32x4_t*)(vp + nn * 512));
 #pragma unroll
         for (int rb = 0; rb < R; ++rb) o[rb][nn] = mfma_16x16x32(af, pf[rb], o[rb][nn]);
@@ -448,10 +438,40 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
         for (int rb = 0; rb < R; ++rb) o[rb][nn] = mfma_16x16x32(af, pf[rb], o[rb][nn]);
       }
     }
+  };
+
+  // prologue: tiles 0 .. S - TB - 1
+  for (int t = 0; t < S - TB; ++t) issue_tile(t, ids_of(t));
+  TileIds cids[TB];
+#pragma unroll
+  for (int u = 0; u < TB; ++u) cids[u] = ids_of(S - TB + u);
+
+  const int nsuper = (np + TB - 1) / TB;
+  for (int jj = 0; jj < nsuper; ++jj) {
+    // this iteration's tiles have landed once at most the copies of later iterations remain
+    wait_vmcnt<kWait>();
+    __syncthreads();
+    {
+      const int tl = np - 1;  // the last tile holds the keys past the context, if any
+      if (tl >= TB * jj && tl < TB * jj + TB && (kt0 + tl) * kTileKeys + kTileKeys > L) {
+        // slots of keys >= L may hold anything, NaN included, and a zero weight does not
+        // cancel a NaN value: zero the values of those keys once, in LDS
+        zero_tail_values<D, KEQV>(smem + (KEQV ? T::kKRing : T::kVRing) + (tl % S) * T::kTile,
+                                  L - (kt0 + tl) * kTileKeys);
+        __syncthreads();
+      }
     }
-    // the next group's tile ids, fetched here (not at the barrier, where every wave of the
-    // workgroup would wait for them at the same moment)
-    gr = group_of(it + 1);
+    // Every wave runs every tile of the workgroup's range: a tile outside a wave's band is
+    // masked whole (its weights are exactly 0) and costs a little matrix-core time, where a
+    // branch around the work would split the copy schedule spread over it.
+    process_tile(TB * jj, std::integral_constant<int, TB>{}, TB * jj + S - TB, cids);
+    if constexpr (TB == 2) {
+      if (TB * jj + 1 < np) process_tile(TB * jj + 1, std::integral_constant<int, 0>{}, 0, cids);
+    }
+    // the next iteration's tile ids, fetched here (not at the barrier, where every wave of
+    // the workgroup would wait for them at the same moment)
+#pragma unroll
+    for (int u = 0; u < TB; ++u) cids[u] = ids_of(TB * (jj + 1) + S - TB + u);
   }
   wait_vmcnt<0>();  // no copy may land in LDS after the workgroup has left it
 
