@@ -36,9 +36,16 @@
  *
  * Paged cache layout (block_size 16, the default page size of vLLM's paged cache; [KUNLUN] §6.3
  * gives the slot arithmetic):
- *   k_cache: [num_blocks][num_kv_heads][16][head_dim]   key rows, head_dim contiguous
+ *   k_cache: [num_blocks][num_kv_heads][16 * head_dim]  one key page per (block, kv head)
  *   v_cache: [num_blocks][num_kv_heads][head_dim][16]   value columns, the 16 keys contiguous
- *   Token position t of sequence b lives in block block_table[b][t / 16], row t % 16.
+ *   Token position t of sequence b lives in block block_table[b][t / 16], row r = t % 16 of
+ *   the page whose logical index in the sequence is lp = t / 16.
+ *   A key page is kept in 16-byte units: unit (row r, x) holds elements x*U .. x*U+U-1 of key
+ *   row r (U = 8 for bf16, 4 for fp32) at unit slot 16*x + (r + 4*(lp % 2)) % 16 of the page,
+ *   i.e. the 16 rows of one unit column are contiguous (256 bytes) and pages of odd logical
+ *   index have their rows rotated by 4.  This is the order in which a 32-key tile (an even
+ *   page, then an odd one) is read by the matrix cores without LDS bank conflicts, so a tile is
+ *   copied to LDS as whole contiguous 1 KiB runs.
  *   The value page is stored transposed so that the matrix-core operand of P.V reads 16
  *   contiguous bytes per lane; with k_eq_v there is no v_cache and values are read from k_cache.
  */

@@ -40,7 +40,10 @@
  *   - Masked keys are left out of the sums (weight exactly 0).
  *
  * Memory layout of the paged cache (the library's documented format):
- *   K page: k_cache[blk][g][off][d]   -- key-major rows, d contiguous.
+ *   K page: k_cache[blk][g][16 rows x D], stored in 16-byte units: unit (row off, x) holds
+ *           elements d = x*U .. x*U+U-1 of key row off (U = 8 for bf16, 4 for fp32) and
+ *           sits at unit slot 16*x + ((off + 4*(lp % 2)) % 16) of the page, lp = pos / 16 being
+ *           the page's logical index in its sequence (rows of odd pages rotated by 4).
  *   V page: v_cache[blk][g][d][off]   -- d-major, the 16 (block_size) keys of a page contiguous.
  *   With k_eq_v the V operand is read from k_cache.
  * dtype code: 0 = fp32 (float storage), 1 = bf16 (uint16_t storage, round-to-nearest-even).
@@ -129,9 +132,16 @@ int64_t ref_slot(const int32_t* block_table, int32_t max_blocks, int32_t req, in
   return b * block_size + o;
 }
 
-/* Element index of K[g][pos][d] of one sequence inside k_cache ([blk][g][off][d]). */
-static int64_t k_index(int64_t blk, int64_t off, int g, int d, int Hkv, int bs, int D) {
-  return ((blk * Hkv + g) * bs + off) * (int64_t)D + d;
+/* Element index of K[g][pos][d] of one sequence inside k_cache: page (blk, g) of bs*D elements,
+ * unit layout described at the top (pos % bs == off; the logical page pos / bs fixes the row
+ * rotation). */
+static int64_t k_index(int64_t blk, int64_t off, int g, int d, int Hkv, int bs, int D, int dtype,
+                       int64_t pos) {
+  const int64_t U = dtype == 1 ? 8 : 4; /* elements per 16-byte unit */
+  const int64_t lp = pos / bs;
+  const int64_t row_slot = (off + 4 * (lp % 2)) % bs;
+  const int64_t unit = (d / U) * bs + row_slot;
+  return (blk * Hkv + g) * bs * (int64_t)D + unit * U + d % U;
 }
 
 /* Element index of V[g][pos][d] inside v_cache ([blk][g][d][off]). */
@@ -209,7 +219,8 @@ int ref_kv_cache_write(int dtype, int Hq, int Hkv, int D, int bs, double rope_th
         for (d = 0; d < D; ++d) x[d] = load_elem(k, dtype, base + d);
         ref_rms_norm(x, wk, D, rms_eps, y);
         ref_rope(y, D, (double)t, rope_theta, z);
-        for (d = 0; d < D; ++d) store_elem(k_cache, dtype, k_index(blk, off, h, d, Hkv, bs, D), z[d]);
+        for (d = 0; d < D; ++d)
+          store_elem(k_cache, dtype, k_index(blk, off, h, d, Hkv, bs, D, dtype, t), z[d]);
         if (!k_eq_v) {
           for (d = 0; d < D; ++d) x[d] = load_elem(v, dtype, base + d);
           ref_rms_norm(x, wv, D, rms_eps, y); /* values are not rotated */
@@ -234,7 +245,7 @@ static void gather(int dtype, int Hkv, int D, int bs, int k_eq_v, const void* k_
     int64_t blk, off;
     ref_slot(block_table, max_blocks, b, j, bs, &blk, &off);
     for (d = 0; d < D; ++d) {
-      K[(j - lo) * D + d] = load_elem(k_cache, dtype, k_index(blk, off, g, d, Hkv, bs, D));
+      K[(j - lo) * D + d] = load_elem(k_cache, dtype, k_index(blk, off, g, d, Hkv, bs, D, dtype, j));
       V[(j - lo) * D + d] = k_eq_v ? K[(j - lo) * D + d]
                                    : load_elem(v_cache, dtype, v_index(blk, off, g, d, Hkv, bs, D));
     }

@@ -64,10 +64,13 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* q, const int
     if (page >= max_blocks) break;
     const int64_t blk = clamp_blk(bt[(int64_t)b * max_blocks + page], num_blocks);
     const int off = key - page * kPage;
-    const float* kr = kc + ((blk * Hkv + g) * kPage + off) * D + lane * C;
+    const float* kp = kc + (blk * Hkv + g) * kPage * D;  // K page (k_page_elem layout)
+    float kv[C];
+#pragma unroll
+    for (int e = 0; e < C; ++e) kv[e] = kp[k_page_elem<4>(off, lane * C + e, page)];
     float part = 0.f;
 #pragma unroll
-    for (int e = 0; e < C; ++e) part = fmaf(qv[e], kr[e], part);
+    for (int e = 0; e < C; ++e) part = fmaf(qv[e], kv[e], part);
 #pragma unroll
     for (int msk = 32; msk >= 1; msk >>= 1) part += __shfl_xor(part, msk, kWave);
     float sc = part * scale;
@@ -78,7 +81,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* q, const int
     l = l * alpha + pw;
 #pragma unroll
     for (int e = 0; e < C; ++e) {
-      const float vv = k_eq_v ? kr[e] : vc[((blk * Hkv + g) * D + lane * C + e) * kPage + off];
+      const float vv = k_eq_v ? kv[e] : vc[((blk * Hkv + g) * D + lane * C + e) * kPage + off];
       o[e] = o[e] * alpha + pw * vv;
     }
     m = m_new;

@@ -82,7 +82,9 @@ __device__ __forceinline__ void decode_piece(const AttnArgs& a, const bf16x8_t (
   };
 
   // page bases are wave-uniform (scalar registers); each lane adds one 32-bit offset
-  const uint32_t koff = (uint32_t)(c16 * D + 8 * j);
+  // K unit (row c16, column 4c + j) of a page of logical parity par: k_page_elem layout
+  const uint32_t koff0 = (uint32_t)(128 * j + 8 * c16);
+  const uint32_t koff1 = (uint32_t)(128 * j + 8 * ((c16 + 4) & 15));
   const uint32_t voff = (uint32_t)(c16 * kPage + 4 * j);
   const int64_t kpage = (int64_t)kPage * D;  // elements per (page, kv head)
   R r;
@@ -91,8 +93,9 @@ __device__ __forceinline__ void decode_piece(const AttnArgs& a, const bf16x8_t (
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const uint16_t* kp = a.kc + (blk_of(s, p) * a.Hkv + head_off) * kpage;
+      const uint32_t koff = ((pbeg + s * NP + p) & 1) ? koff1 : koff0;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) r.k[p][c] = ld16(kp + koff + 32 * c);
+      for (int c = 0; c < NC; ++c) r.k[p][c] = ld16(kp + koff + 512 * c);
     }
   };
   auto issue_v = [&](int s) {

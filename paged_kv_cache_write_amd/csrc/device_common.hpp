@@ -73,6 +73,21 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
   return f32_to_bf16(__uint_as_float(u));
 }
 
+// ------------------------------------------------------------------------ K page layout -----
+// A K page (16 keys of one kv head) is stored in 16-byte units: unit (row r, x) holds elements
+// [x U, x U + U) of key row r, U = 16 / element size (8 for bf16, 4 for fp32), and sits at
+// byte 256 x + 16 ((r + 4 (lp mod 2)) mod 16) of the page, lp being the page's logical index
+// (position / 16) in its sequence.  So the 16 rows of one unit column x form one 256-byte
+// run, a 1 KiB run holds four consecutive unit columns of all 16 rows, and pages of odd
+// logical index have their rows rotated by 4: a 32-key tile (an even page, then an odd one)
+// copied to LDS as it is stored lets the 16 lanes of a matrix-core fragment read (8 rows of
+// each page, one unit column) hit 16 distinct bank groups.
+template <int ESIZE>
+__device__ __forceinline__ int64_t k_page_elem(int r, int d, int64_t lp) {
+  constexpr int U = 16 / ESIZE;
+  return (int64_t)(d / U) * (16 * U) + (int64_t)((r + 4 * (int)(lp & 1)) & 15) * U + (d % U);
+}
+
 // ------------------------------------------------------------------------ MFMA --------------
 
 __device__ __forceinline__ float4_t mfma_16x16x32(const bf16x8_t& a, const bf16x8_t& b,

@@ -15,7 +15,8 @@
 // Sources: [KUNLUN] = "Gemma 4 模型架构解析" (vLLM-Kunlun adaptation guide), §4.3 (a layer that
 // owns its cache norms k, rotates q and k, norms v), §6.3 (slot = page id * 16 + row), §6.4
 // (per-token scatter into the cache).  [MNN] = "MNN 支持 Gemma4 全系列", §6.1 (q, k and v norms).
-// Layout of the pages: K [blk][g][row][d]; V [blk][g][d][row] (transposed page).
+// Layout of the pages: K [blk][g] in 16-byte units, chunk-major, rows rotated by 4 on odd
+// logical pages (k_page_elem); V [blk][g][d][row] (transposed page).
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -184,11 +185,12 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
           Elem<T>::store(a.q, r.base + H + lane * C + i, x2[i]);
         }
       } else if (r.kind == 1) {
-        const int64_t row = ((blk * a.Hkv + r.h) * kPage + off) * D;
+        const int64_t pg = (blk * a.Hkv + r.h) * (int64_t)D * kPage;
 #pragma unroll
         for (int i = 0; i < C; ++i) {
-          Elem<T>::store(a.kc, row + lane * C + i, x1[i]);
-          Elem<T>::store(a.kc, row + H + lane * C + i, x2[i]);
+          Elem<T>::store(a.kc, pg + k_page_elem<sizeof(T)>((int)off, lane * C + i, page), x1[i]);
+          Elem<T>::store(a.kc, pg + k_page_elem<sizeof(T)>((int)off, H + lane * C + i, page),
+                         x2[i]);
         }
       } else {
         const int64_t pg = (blk * a.Hkv + r.h) * (int64_t)D * kPage;

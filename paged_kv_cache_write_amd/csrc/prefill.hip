@@ -14,9 +14,12 @@
 // at head size 512) with Q^T and the O^T accumulators in registers.  Key tiles of 32 keys (two
 // pages) are copied from HBM straight into LDS by global_load_lds_dwordx4 (no registers
 // involved) through rings of K and V^T tiles (4 stages each, 2 at head size 512); one barrier
-// per tile both publishes a tile and frees a stage.  A wave's copies for a later tile are
-// spread over the matrix-core instructions of the current one (K copies among the QK^T
-// products, V copies among the P.V products) instead of queueing behind the barrier.  Block
+// per tile both publishes a tile and frees a stage.  Every copy reads one contiguous 1 KiB
+// run (K pages are stored in the order LDS wants them, see below).  A wave's copies for a
+// later tile are spread over the matrix-core instructions of the current one (K copies among
+// the QK^T products, V copies among the P.V products) instead of queueing behind the barrier.
+// Operand fragments are read from LDS kPF fragments ahead of the products that use them: the
+// loops are cut into one chunk per fragment by scheduling fences.  Block
 // ids come through the scalar cache, one load per tile, fetched at the end of the previous
 // iteration.  Only tiles that intersect the band [past + i - W + 1, past + i] of some row of
 // the workgroup are visited, and every wave runs all of them (a tile outside a wave's rows is
@@ -31,11 +34,15 @@
 // of P.V without moving between lanes, and the matching V^T operand is one 16-byte read.
 //
 // LDS layouts (per page of 16 keys), chosen so that every operand read is one base register
-// plus an immediate offset, is free of bank conflicts, and still arrives as whole 16-byte
-// pieces from HBM:
+// plus an immediate offset and is free of bank conflicts; both are the pages' HBM layouts, so
+// a tile arrives by plain contiguous copies:
 //   K page  chunk-major: the 16-byte chunk x (elements 8x .. 8x+7) of key row r of page p is
 //           stored at byte 256 x + 16 ((r + 4p) mod 16), so a QK^T fragment read by 16 lanes
-//           (16 distinct rows, one chunk) covers 16 distinct bank groups.
+//           (16 distinct rows, one chunk) covers 16 distinct bank groups.  p is the page's
+//           place in the tile, which is the parity of its logical index (tiles start at even
+//           pages): the cache's K page layout (k_page_elem).  Measured: 1 KiB copies gathered
+//           as 16 rows x 64 bytes (what a row-major HBM page needs) move a third of the bytes
+//           per clock that contiguous 1 KiB copies move.
 //   V^T page [D rows][16 keys] (32 bytes a row), rows in order: the 16 lanes of a lane group
 //           read 16 consecutive rows, one half each (measured conflict-free; swapping the halves
 //           of every other group of 8 rows makes the read 2-way conflicted).
@@ -45,13 +52,13 @@
 // Order of work: workgroup ids are dealt to the 8 XCDs round robin, so consecutive logical
 // tiles are given to one XCD (its L2 then serves the key tiles shared by neighbouring row
 // tiles), and within a (sequence, kv head) the row tiles with the most keys start first.
-#include "attn_common.hpp"
+#include "prefill_common.hpp"
 
 namespace ga {
 namespace {
 
-constexpr int kTileKeys = 2 * kPage;  // 32 keys per tile: P.V runs on 16x16x32 MFMAs
 constexpr int kWaves = 8;             // two waves per SIMD, 256 registers each
+constexpr int kPF = 3;                // operand fragment reads in flight ahead of their products
 
 // MFMA column blocks per wave: 2 (32 rows) up to head size 256, 1 (16 rows) at 512, where
 // 32 rows of Q^T (128 registers) plus O^T (256) would not fit a wave's 256 registers.
@@ -86,67 +93,22 @@ struct TileLds {
   static_assert(kBytes <= kBudget, "LDS budget");
 };
 
-// Row of page c16 / 8 that QK^T product m (0, 1) places at MFMA row c16: keys {0-3, 8-11} of
-// each page for m = 0 and {4-7, 12-15} for m = 1.
-__device__ __forceinline__ int qk_row_key(int c16, int m) {
-  return (c16 & 3) + 8 * ((c16 >> 2) & 1) + 4 * m;
-}
-
-// One HBM -> LDS copy of 1 KiB: each lane moves 16 bytes to M0 + 16 * lane.  Issued through
-// inline assembly so that the compiler does not add waits of its own for the LDS it writes:
-// the kernel waits on the vector-memory counter explicitly before the barrier that
-// publishes a tile.  No memory clobber: a copy only ever writes a ring stage that no LDS
-// access of the same iteration touches, and being volatile it stays ordered with the
-// barriers and explicit waits that separate iterations.
-__device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds_off) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(lds_off)
-               : "m0");
-}
-
-// Two consecutive int32 (wave-uniform address) through the scalar cache, waited for inside the
-// same statement so the value is complete when the statement ends.  Used only where no LDS
-// read of this wave is outstanding (the wait covers those too).
-__device__ __forceinline__ int2 scalar_load2(const int32_t* p) {
-  int2 v;
-  asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
-  return v;
-}
-__device__ __forceinline__ int scalar_load1(const int32_t* p) {
-  int v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
-  return v;
-}
-
-// Wait until at most N vector-memory operations of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 // Copy i (0 .. kPerWave-1) of this wave for one tile of K (V=false) or of V^T (V=true) into
-// `lds_off`: 1 KiB chunk wave + kWaves * i of the tile.
+// `lds_off`: 1 KiB chunk q = wave + kWaves * i of the tile, from a wave-uniform base plus the
+// per-lane offset 16 lane.  Both page kinds are copied as they are stored (K pages already hold
+// the LDS arrangement: k_page_elem), so every copy reads one contiguous 1 KiB run.
 template <int D, bool KEQV, bool V>
 __device__ __forceinline__ void issue_chunk(const AttnArgs& a, uint32_t lds_off, int g,
-                                            int64_t blkA, int64_t blkB, int wave, int lane,
-                                            int i) {
+                                            int64_t blkA, int64_t blkB, int wave, int i,
+                                            uint32_t vlane) {
   using T = TileLds<D, KEQV>;
   constexpr int kChunksPerPage = T::kPageBytes / 1024;
-  const int q = wave + kWaves * i;  // 1 KiB chunk of the tile
+  const int q = wave + kWaves * i;  // 1 KiB chunk of the tile (wave-uniform)
   const int page = q / kChunksPerPage, qq = q - page * kChunksPerPage;
-  const int s = qq * 64 + lane;     // 16-byte slot inside the page
   const int64_t blk = page ? blkB : blkA;
-  const void* src;
-  if constexpr (!V) {
-    const int x = s >> 4, r = ((s & 15) - 4 * page) & 15;  // chunk-major, rotated by 4 page
-    src = a.kc + ((blk * a.Hkv + g) * kPage + r) * D + x * 8;
-  } else {
-    const int d = s >> 1, h = s & 1;
-    src = a.vc + ((blk * a.Hkv + g) * D + d) * kPage + h * 8;
-  }
-  lds_copy16(src, __builtin_amdgcn_readfirstlane(lds_off + q * 1024));
+  const int64_t page_bytes = ((blk * a.Hkv + g) * kPage * D) * 2;
+  const unsigned char* base = (const unsigned char*)(V ? (const void*)a.vc : (const void*)a.kc);
+  lds_copy16_sv(base + page_bytes + 1024 * qq, vlane, lds_off + q * 1024);
 }
 
 // Zero, in one staged tile, the values of key slots nvalid .. 31 (keys past the context):
@@ -176,7 +138,7 @@ __device__ __forceinline__ void zero_tail_values(unsigned char* tile, int nvalid
   }
 }
 
-template <int D, bool CAP, bool KEQV>
+template <int D, int SM, bool KEQV>
 __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs a, int tiles_per_bg,
                                                                      int n_tiles) {
   using T = TileLds<D, KEQV>;
@@ -308,14 +270,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
   static_assert(S % TB == 0 && S >= 2 * TB, "ring depth");
   constexpr int kPerTile = T::kPerWave * (KEQV ? 1 : 2);
   constexpr int kWait = (S / TB - 2) * TB * kPerTile;  // copies of later iterations in flight
+  const uint32_t vlane = 16u * lane;
   auto k_chunk = [&](int t, const TileIds& ids, int i) {
     issue_chunk<D, KEQV, false>(a, smem_off + T::kKRing + (t % S) * T::kTile, g, ids.a, ids.b,
-                                wave, lane, i);
+                                wave, i, vlane);
   };
   auto v_chunk = [&](int t, const TileIds& ids, int i) {
     if constexpr (!KEQV)
       issue_chunk<D, KEQV, true>(a, smem_off + T::kVRing + (t % S) * T::kTile, g, ids.a,
-                                 ids.b, wave, lane, i);
+                                 ids.b, wave, i, vlane);
   };
   auto issue_tile = [&](int t, const TileIds& ids) {
 #pragma unroll
@@ -330,24 +293,40 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
     constexpr int Q = decltype(ncp)::value * T::kPerWave;  // copies of each ring
     const int k0 = (kt0 + t) * kTileKeys;
     const unsigned char* kt = smem + T::kKRing + (t % S) * T::kTile;
+    const unsigned char* vt = smem + T::kVRing + (t % S) * T::kTile + voff;
 
-    // ---- S^T = K Q^T: s[m][rb], product m covering the key rows described above
+    // ---- S^T = K Q^T: s[m][rb], product m covering the key rows described above.  One
+    // chunk per K fragment f (c = f / 2, m = f % 2): its R products, the read of fragment
+    // f + kPF and a share of the tile copies; the fences keep the reads kPF fragments ahead of
+    // the products that use them.
     float4_t s[2][R];
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int rb = 0; rb < R; ++rb) s[m][rb] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-#pragma unroll
-      for (int q = c * Q / NC; q < (c + 1) * Q / NC; ++q)
+    bf16x8_t kf[2 * NC];
+    sfor<kPF>([&](auto fc) {
+      constexpr int f = decltype(fc)::value;
+      kf[f] = as_bf16x8(*(const u32x4_t*)(kt + koff[f & 1] + 1024 * (f >> 1)));
+    });
+    sfor<2 * NC>([&](auto fc) {
+      constexpr int f = decltype(fc)::value;
+      if constexpr (f + kPF < 2 * NC)
+        kf[f + kPF] =
+            as_bf16x8(*(const u32x4_t*)(kt + koff[(f + kPF) & 1] + 1024 * ((f + kPF) >> 1)));
+      sfor<(f + 1) * Q / (2 * NC) - f * Q / (2 * NC)>([&](auto qc) {
+        constexpr int q = f * Q / (2 * NC) + decltype(qc)::value;
         k_chunk(ct + q / T::kPerWave, cids[q / T::kPerWave], q % T::kPerWave);
+      });
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const bf16x8_t kf = as_bf16x8(*(const u32x4_t*)(kt + koff[m] + 1024 * c));
-#pragma unroll
-        for (int rb = 0; rb < R; ++rb) s[m][rb] = mfma_16x16x32(kf, qf[rb][c], s[m][rb]);
-      }
+      for (int rb = 0; rb < R; ++rb)
+        s[f & 1][rb] = mfma_16x16x32(kf[f], qf[rb][f >> 1],
+                                     f < 2 ? float4_t{0.f, 0.f, 0.f, 0.f} : s[f & 1][rb]);
+      fence_sched();
+    });
+    // the first V^T fragments of this tile's P.V, read while the softmax runs
+    bf16x8_t vf[ND];
+    if constexpr (!KEQV) {
+      sfor<kPF>([&](auto nc) {
+        constexpr int nn = decltype(nc)::value;
+        vf[nn] = as_bf16x8(*(const u32x4_t*)(vt + nn * 512));
+      });
     }
 
     // ---- scores on the log2 scale, band + causal mask (skipped when the whole tile is
@@ -357,7 +336,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
 #pragma unroll
     for (int rb = 0; rb < R; ++rb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) xs[rb][e] = to_log2<CAP>(s[e >> 2][rb][e & 3], a.sc);
+      for (int e = 0; e < 8; ++e) xs[rb][e] = score_in<SM>(s[e >> 2][rb][e & 3], a.sc);
     if (!full) {
       const int kk = k0 + kslot;
 #pragma unroll
@@ -368,22 +347,20 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
           xs[rb][e] = (uint32_t)(d0 + e) <= span_c[rb] ? xs[rb][e] : -INFINITY;
       }
     }
-    // ---- online softmax with a lazily moved reference: the reference moves only when a
-    // weight would exceed 2^8, so most tiles skip the rescale of O
+    // ---- online softmax with a lazily moved reference (kLazyLog2), so most tiles skip the
+    // rescale of O
     bool need = false;
     float mx[R];
 #pragma unroll
     for (int rb = 0; rb < R; ++rb) {
-      float m = fmaxf(fmaxf(fmaxf(xs[rb][0], xs[rb][1]), fmaxf(xs[rb][2], xs[rb][3])),
-                      fmaxf(fmaxf(xs[rb][4], xs[rb][5]), fmaxf(xs[rb][6], xs[rb][7])));
-      m = max_over_groups(m);
+      const float m = score_max<SM>(max_over_groups_nc(max8_nc(xs[rb])), a.sc);
       mx[rb] = m;
-      need |= m > m_ref[rb] + 8.0f;
+      need |= m > m_ref[rb] + kLazyLog2;
     }
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
       for (int rb = 0; rb < R; ++rb) {
-        const float m_new = mx[rb] > m_ref[rb] + 8.0f ? mx[rb] : m_ref[rb];
+        const float m_new = mx[rb] > m_ref[rb] + kLazyLog2 ? mx[rb] : m_ref[rb];
         const float alpha = m_ref[rb] == -INFINITY ? 1.f : fast_exp2(m_ref[rb] - m_new);
         l_run[rb] *= alpha;
 #pragma unroll
@@ -398,7 +375,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
       bf16x2_t pw[4];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        pw[w] = cvt_bf16x2(fast_exp2(xs[rb][2 * w] - mu), fast_exp2(xs[rb][2 * w + 1] - mu));
+        pw[w] = cvt_bf16x2(fast_exp2(score_exp_arg<SM>(xs[rb][2 * w], mu, a.sc)),
+                           fast_exp2(score_exp_arg<SM>(xs[rb][2 * w + 1], mu, a.sc)));
         // the row sum uses the same bf16-rounded weights that multiply V
         l_run[rb] = sum_bf16x2(pw[w], l_run[rb]);
       }
@@ -406,18 +384,20 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
                         pw[2][0], pw[2][1], pw[3][0], pw[3][1]};
     }
 
-    // ---- O^T[d][row] += V^T[d][keys] P^T[keys][row]
+    // ---- O^T[d][row] += V^T[d][keys] P^T[keys][row], one chunk per V^T fragment
     if constexpr (!KEQV) {
-      const unsigned char* vp = smem + T::kVRing + (t % S) * T::kTile + voff;
-#pragma unroll
-      for (int nn = 0; nn < ND; ++nn) {
-#pragma unroll
-        for (int q = nn * Q / ND; q < (nn + 1) * Q / ND; ++q)
+      sfor<ND>([&](auto nc) {
+        constexpr int nn = decltype(nc)::value;
+        if constexpr (nn + kPF < ND)
+          vf[nn + kPF] = as_bf16x8(*(const u32x4_t*)(vt + (nn + kPF) * 512));
+        sfor<(nn + 1) * Q / ND - nn * Q / ND>([&](auto qc) {
+          constexpr int q = nn * Q / ND + decltype(qc)::value;
           v_chunk(ct + q / T::kPerWave, cids[q / T::kPerWave], q % T::kPerWave);
-        const bf16x8_t af = as_bf16x8(*(const u32x4_t*)(vp + nn * 512));
+        });
 #pragma unroll
-        for (int rb = 0; rb < R; ++rb) o[rb][nn] = mfma_16x16x32(af, pf[rb], o[rb][nn]);
-      }
+        for (int rb = 0; rb < R; ++rb) o[rb][nn] = mfma_16x16x32(vf[nn], pf[rb], o[rb][nn]);
+        fence_sched();
+      });
     } else {
       // values are the keys: gather K[key][d] column-wise from the chunk-major K page;
       // key 8 (j % 2) + e of page j / 2 at d = 16 nn + c16
@@ -494,7 +474,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
   }
 }
 
-template <int D, bool CAP, bool KEQV>
+template <int D, int SM, bool KEQV>
 hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   using T = TileLds<D, KEQV>;
   constexpr int kRowsPerWg = Rows<D>::kPerWg;
@@ -504,18 +484,25 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   const int grid = (n_tiles + 7) / 8 * 8;  // whole rounds over the 8 XCDs
   static_assert(T::kBytes <= 160 * 1024, "LDS budget");
   hipError_t e = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&prefill_tiled_kernel<D, CAP, KEQV>),
+      reinterpret_cast<const void*>(&prefill_tiled_kernel<D, SM, KEQV>),
       hipFuncAttributeMaxDynamicSharedMemorySize, T::kBytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((prefill_tiled_kernel<D, CAP, KEQV>), dim3(grid), dim3(64 * kWaves),
+  hipLaunchKernelGGL((prefill_tiled_kernel<D, SM, KEQV>), dim3(grid), dim3(64 * kWaves),
                      T::kBytes, s, a, tiles_per_bg, n_tiles);
   return hipGetLastError();
 }
 
+template <int D, int SM>
+hipError_t by_keqv(const AttnArgs& a, bool keqv, hipStream_t s) {
+  return keqv ? launch_t<D, SM, true>(a, s) : launch_t<D, SM, false>(a, s);
+}
+
 template <int D>
 hipError_t by_flags(const AttnArgs& a, bool cap, bool keqv, hipStream_t s) {
-  if (cap) return keqv ? launch_t<D, true, true>(a, s) : launch_t<D, true, false>(a, s);
-  return keqv ? launch_t<D, false, true>(a, s) : launch_t<D, false, false>(a, s);
+  if (cap) return by_keqv<D, kScoreCap>(a, keqv, s);
+  // a positive scale commutes with the max, so it can be applied inside the exponent
+  return a.sc.c_scale > 0.f ? by_keqv<D, kScoreFold>(a, keqv, s)
+                            : by_keqv<D, kScorePlain>(a, keqv, s);
 }
 
 }  // namespace

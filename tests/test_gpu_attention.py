@@ -7,6 +7,7 @@ import torch
 import paged_kv_cache_write_amd as ga
 import workloads as wl
 from harness import PagedCase, assert_attn_close, assert_same_result, i32
+from layout import logical_k, unit_elems
 
 pytestmark = pytest.mark.gpu
 
@@ -184,7 +185,8 @@ def test_k_eq_v_equals_separate_caches_holding_the_same_tensor():
     spec2 = wl.LayerSpec("bf16", 16, 2, 512, window=0, k_eq_v=False, rope_theta=1e6)
     case2 = PagedCase(spec2, pb, 71)
     case2.kc.copy_(case.kc)
-    case2.vc.copy_(case.kc.transpose(2, 3))
+    # the same tensor in the V page layout: K's logical rows (tests/layout.py), transposed
+    case2.vc.copy_(logical_k(case.kc, pb.block_table, lens, unit_elems("bf16")).transpose(2, 3))
     b = case2.prefill(qd, cu, cl)
     torch.cuda.synchronize()
     assert_same_result(a, b)

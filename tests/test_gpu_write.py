@@ -5,6 +5,7 @@ import torch
 
 import workloads as wl
 from harness import PagedCase, ulp_distance
+from layout import logical_k, unit_elems
 
 pytestmark = pytest.mark.gpu
 
@@ -80,6 +81,7 @@ def test_only_owned_slots_change():
     case.write(lens, news, 14)
     torch.cuda.synchronize()
     kc, vc = case.host_caches()
+    kc = logical_k(kc, pb.block_table, lens, unit_elems("bf16"))  # rows of used pages in order
     written_k = np.zeros(kc.shape[:3], bool)
     for b, (L, n) in enumerate(zip(lens, news)):
         for t in range(L - n, L):

@@ -17,6 +17,7 @@ import torch
 
 import oracle
 from oracle import BF16, FP32
+from layout import logical_k, page_rows, put_k_rows, unit_elems
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 BS = 16
@@ -33,8 +34,9 @@ def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
 def make_paged(K, V, seed, spare=3):
     """Scatter contiguous per-sequence K[b] [Hkv,L_b,D] / V[b] into the documented page layout.
 
-    Written independently of the oracle with numpy fancy indexing: K pages [blk][g][off][d],
-    V pages [blk][g][d][off].  Returns (k_cache, v_cache, block_table) as float32 arrays."""
+    Written independently of the oracle with numpy fancy indexing: K pages in the 16-byte unit
+    layout (tests/layout.py, fp32 units of 4), V pages [blk][g][d][off].  Returns (k_cache,
+    v_cache, block_table) as float32 arrays."""
     rng = np.random.default_rng(seed)
     Hkv, _, D = K[0].shape
     need = [-(-k.shape[1] // BS) for k in K]
@@ -53,7 +55,7 @@ def make_paged(K, V, seed, spare=3):
         blk = bt[b, j // BS]
         off = j % BS
         for g in range(Hkv):
-            kc[blk, g, off, :] = k[g]
+            put_k_rows(kc, blk, g, j, k[g], unit_elems("fp32"))
             vc[blk, g, :, off] = v[g]
     return kc, vc, bt
 
@@ -231,7 +233,10 @@ def test_plain_scatter_is_bit_exact_both_dtypes():
             for i in range(n[b]):
                 t = past + i
                 blk, off = bt[b, t // BS], t % BS
-                np.testing.assert_array_equal(kc[blk, :, off, :], k[cu[b] + i])
+                for g in range(Hkv):
+                    rows = page_rows(kc[blk, g].reshape(-1), D, unit_elems(
+                        "bf16" if dt == BF16 else "fp32"), (t // BS) % 2)
+                    np.testing.assert_array_equal(rows[off], k[cu[b] + i, g])
                 np.testing.assert_array_equal(vc[blk, :, :, off], v[cu[b] + i])
 
 
@@ -265,8 +270,9 @@ def test_write_norm_then_rope_on_q_k_not_v():
         t = 33 + i
         blk, off = bt[0, t // BS], t % BS
         np.testing.assert_allclose(q_out[i], rot(norm(q[i], ws[0]), t), rtol=2e-7, atol=2e-7)
-        np.testing.assert_allclose(kc[blk, :, off, :], rot(norm(k[i], ws[1]), t), rtol=2e-7,
-                                   atol=2e-7)
+        krow = np.stack([page_rows(kc[blk, g].reshape(-1), D, unit_elems("fp32"),
+                                   (t // BS) % 2)[off] for g in range(Hkv)])
+        np.testing.assert_allclose(krow, rot(norm(k[i], ws[1]), t), rtol=2e-7, atol=2e-7)
         np.testing.assert_allclose(vc[blk, :, :, off], norm(v[i], ws[2]), rtol=2e-7, atol=2e-7)
 
 
@@ -286,7 +292,8 @@ def test_write_positions_follow_context_lens():
                           bt, kc, vc)
     for b, poss in ((0, range(46, 50)), (1, range(0, 3))):
         for t in poss:
-            row = kc[bt[b, t // BS], 0, t % BS]
+            row = page_rows(kc[bt[b, t // BS], 0].reshape(-1), D, unit_elems("fp32"),
+                            (t // BS) % 2)[t % BS]
             assert abs(row[0] - math.cos(t)) < 1e-7 and abs(row[D // 2] - math.sin(t)) < 1e-7
 
 
@@ -412,7 +419,8 @@ def test_softcap_large_cap_tends_to_uncapped():
 def test_k_eq_v_equals_separate_cache_holding_the_same_tensor():
     rng = np.random.default_rng(15)
     K, V, kc, vc, bt, q, cu, cl, n = _rand_case(rng)
-    vc_from_k = np.ascontiguousarray(np.swapaxes(kc, 2, 3))  # same tensor, V page layout
+    # the same tensor in the V page layout: K's logical rows, transposed per page
+    vc_from_k = np.ascontiguousarray(np.swapaxes(logical_k(kc, bt, cl, unit_elems("fp32")), 2, 3))
     a = run_attn(kc, None, bt, q, cu, cl, 2, window=9, k_eq_v=1)
     b = run_attn(kc, vc_from_k, bt, q, cu, cl, 2, window=9, k_eq_v=0)
     np.testing.assert_array_equal(a, b)
