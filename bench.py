@@ -84,7 +84,8 @@ def log(*a):
 def params(spec):
     return ga.layer_params(spec.dtype, spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
                            window=spec.window, scale=spec.scale, softcap=spec.softcap,
-                           k_eq_v=spec.k_eq_v, rope_theta=spec.rope_theta, rms_eps=spec.rms_eps)
+                           k_eq_v=spec.k_eq_v, rope_theta=spec.rope_theta, rms_eps=spec.rms_eps,
+                           rope_angles=spec.rope_angles, rope_scale=spec.rope_scale)
 
 
 def i32(a, dev):

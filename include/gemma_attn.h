@@ -90,13 +90,23 @@ typedef struct {
                            v_norm_w must then be NULL */
   float rope_theta;     /* RoPE base (1e4 sliding, 1e6 global); 0: no rotation; < 0 invalid */
   float rms_eps;        /* RMSNorm epsilon, >= 0 (Gemma layers use 1e-6) */
+  int32_t rope_angles;  /* rotated frequency pairs n ([KUNLUN] 挑战 5, proportional RoPE): pair k
+                           (dimensions k and k + D/2) turns by t * theta^(-2k/D) for k < n and
+                           not at all for k >= n; 0 (or D/2) rotates every pair; < 0 or > D/2
+                           invalid */
+  float rope_scale;     /* linear RoPE scaling ([INFLM] follow-up list: Gemma-3 global layers use
+                           a linear factor, e.g. 8): the angle uses t / rope_scale instead of t;
+                           0 means 1; < 0 or non-finite invalid */
 } ga_layer_params;
 
 /* Norm + rotate + scatter the new tokens of a batch ([KUNLUN] §4.3 forward of a layer that
  * owns its cache: k_norm, RoPE on q and k, v_norm; §6.3-6.4 slot and write path; [MNN] §6.1).
  *   q            DEVICE [total_tokens][Hq][D]   raw query in; normalised and rotated query out
  *                (in place).  May be NULL (only k/v are written).
- *   k            DEVICE [total_tokens][Hkv][D]  raw keys.
+ *   k            DEVICE [total_tokens][Hkv][D]  raw keys.  NULL: a layer that reads another
+ *                layer's cache ([KUNLUN] §4, YOCO KV sharing: only q is normed and rotated);
+ *                q must then be given, v, k_norm_w and v_norm_w must be NULL, and nothing is
+ *                stored (block_table, k_cache and v_cache may be NULL and are not read).
  *   v            DEVICE [total_tokens][Hkv][D]  raw values; NULL iff k_eq_v.
  *   q_norm_w,
  *   k_norm_w,
@@ -108,8 +118,9 @@ typedef struct {
  *                take positions context_lens[b] - n_b .. context_lens[b] - 1.
  *   block_table  DEVICE int32 [batch][max_blocks].
  *   k_cache, v_cache  DEVICE, layouts above; v_cache NULL iff k_eq_v.  num_blocks = pages in each.
- * Rotation: pair (k, k + D/2) turns by angle t * theta^(-2k/D), with the angle formed and the
- * whole norm + rotation evaluated in double precision and rounded once into the storage type.
+ * Rotation: pair (k, k + D/2) turns by angle (t / rope_scale) * theta^(-2k/D) for k <
+ * rope_angles (all pairs by default), with the angle formed and the whole norm + rotation
+ * evaluated in double precision and rounded once into the storage type.
  * Values are normalised but never rotated. */
 ga_status ga_kv_cache_write(const ga_layer_params* p, void* q, const void* k, const void* v,
                             const float* q_norm_w, const float* k_norm_w, const float* v_norm_w,

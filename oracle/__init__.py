@@ -53,9 +53,10 @@ def _load():
         lib.ref_rms_norm.restype = None
         lib.ref_rms_norm.argtypes = [P, P, ctypes.c_int, dbl, P]
         lib.ref_rope.restype = None
-        lib.ref_rope.argtypes = [P, ctypes.c_int, dbl, dbl, P]
+        lib.ref_rope.argtypes = [P, ctypes.c_int, dbl, dbl, ctypes.c_int, dbl, P]
         lib.ref_kv_cache_write.restype = ctypes.c_int
-        lib.ref_kv_cache_write.argtypes = [ctypes.c_int] * 5 + [dbl, dbl, ctypes.c_int] + [P] * 6 \
+        lib.ref_kv_cache_write.argtypes = [ctypes.c_int] * 5 + [dbl, ctypes.c_int, dbl, dbl,
+                                                                ctypes.c_int] + [P] * 6 \
             + [P, P, P, i32, i32, P, P]
         lib.ref_attention.restype = ctypes.c_int
         lib.ref_attention.argtypes = [ctypes.c_int] * 6 + [dbl, dbl, ctypes.c_int, P, P, P, P, P,
@@ -116,18 +117,25 @@ def rms_norm(x: np.ndarray, w: np.ndarray | None, eps: float) -> np.ndarray:
     return y
 
 
-def rope(x: np.ndarray, t: float, theta: float) -> np.ndarray:
+def rope(x: np.ndarray, t: float, theta: float, angles: int = 0, pos_scale: float = 1.0) -> np.ndarray:
+    """Rotate-half RoPE of one vector at position t; `angles` rotated frequency pairs (0 = all),
+    position divided by `pos_scale`."""
     x = np.ascontiguousarray(x, dtype=np.float64)
     y = np.empty_like(x)
-    _load().ref_rope(_p(x), x.shape[-1], float(t), float(theta), _p(y))
+    D = x.shape[-1]
+    a = angles if 0 < angles < D // 2 else D // 2
+    _load().ref_rope(_p(x), D, float(t), float(theta), int(a), float(pos_scale), _p(y))
     return y
 
 
 # ------------------------------------------------------------------ entry points ----------
 
 def kv_cache_write(dtype, Hq, Hkv, D, rope_theta, rms_eps, k_eq_v, q, k, v, wq, wk, wv,
-                   cu_seqlens, context_lens, block_table, k_cache, v_cache, block_size=16):
-    """Norm + RoPE + scatter in double; updates q (if given), k_cache and v_cache in place."""
+                   cu_seqlens, context_lens, block_table, k_cache, v_cache, block_size=16,
+                   rope_angles=0, rope_scale=0.0):
+    """Norm + RoPE + scatter in double; updates q (if given), k_cache and v_cache in place.
+    k = v = None: q only (a layer sharing another layer's cache); rope_angles: rotated
+    frequency pairs (0 = all); rope_scale: position divisor (0 = 1)."""
     et = _elem(dtype)
     q = _check(q, et, "q")
     k = _check(k, et, "k")
@@ -140,6 +148,7 @@ def kv_cache_write(dtype, Hq, Hkv, D, rope_theta, rms_eps, k_eq_v, q, k, v, wq, 
     cl = _check(np.ascontiguousarray(context_lens, np.int32), np.int32, "context_lens")
     bt = _check(np.ascontiguousarray(block_table, np.int32), np.int32, "block_table")
     rc = _load().ref_kv_cache_write(dtype, Hq, Hkv, D, block_size, float(rope_theta),
+                                    int(rope_angles), float(rope_scale),
                                     float(rms_eps), int(k_eq_v), _p(q), _p(k), _p(v), _p(wq),
                                     _p(wk), _p(wv), _p(cu), _p(cl), _p(bt), bt.shape[1],
                                     cl.shape[0], _p(k_cache), _p(v_cache))

@@ -164,17 +164,21 @@ void ref_rms_norm(const double* x, const float* w, int D, double eps, double* y)
   for (d = 0; d < D; ++d) y[d] = x[d] * inv * (double)w[d];
 }
 
-/* Rotary embedding at position t, rotate-half pairing (k, k + D/2), frequency
- * omega_k = 1 / theta^(2k / D).  theta <= 0: identity. */
-void ref_rope(const double* x, int D, double t, double theta, double* y) {
+/* Rotary embedding at position t, rotate-half pairing (k, k + D/2).
+ * [KUNLUN] 挑战 5 (proportional RoPE): the frequency of pair k is 1 / theta^(2k / D) -- the
+ * exponent's denominator is the head size -- for the first `angles` pairs, and 0 (no rotation)
+ * for the rest; angles = D/2 is the full rotation.  [INFLM] follow-up list (linear RoPE
+ * scaling): the position enters as t / pos_scale.  theta <= 0: identity. */
+void ref_rope(const double* x, int D, double t, double theta, int angles, double pos_scale,
+              double* y) {
   int k, half = D / 2;
   if (theta <= 0.0) {
     for (k = 0; k < D; ++k) y[k] = x[k];
     return;
   }
   for (k = 0; k < half; ++k) {
-    double omega = 1.0 / pow(theta, (2.0 * k) / (double)D);
-    double a = t * omega, c = cos(a), s = sin(a);
+    double omega = k < angles ? 1.0 / pow(theta, (2.0 * k) / (double)D) : 0.0;
+    double a = (t / pos_scale) * omega, c = cos(a), s = sin(a);
     y[k] = x[k] * c - x[k + half] * s;
     y[k + half] = x[k + half] * c + x[k] * s;
   }
@@ -182,16 +186,21 @@ void ref_rope(const double* x, int D, double t, double theta, double* y) {
 
 /* Norm, rotate and scatter the new tokens of every sequence.
  *   q: [T][Hq][D] raw in, written back normalised and rotated (may be NULL);
- *   k, v: [T][Hkv][D] raw (v NULL iff k_eq_v);
+ *   k, v: [T][Hkv][D] raw (v NULL iff k_eq_v); k and v both NULL: a layer that shares another
+ *   layer's cache ([KUNLUN] §4.3: only q is normed and rotated, nothing is stored);
+ *   rope_angles: rotated frequency pairs (0 = all D/2); rope_scale: position divisor (0 = 1);
  *   cu_seqlens[B+1]: offsets of each sequence's new tokens; context_lens[B]: length after the
  *   write, so the new tokens of sequence b sit at positions context_lens[b] - n_b ... */
 int ref_kv_cache_write(int dtype, int Hq, int Hkv, int D, int bs, double rope_theta,
-                       double rms_eps, int k_eq_v, void* q, const void* k, const void* v,
+                       int rope_angles, double rope_scale, double rms_eps, int k_eq_v, void* q,
+                       const void* k, const void* v,
                        const float* wq, const float* wk, const float* wv,
                        const int32_t* cu_seqlens, const int32_t* context_lens,
                        const int32_t* block_table, int32_t max_blocks, int32_t batch,
                        void* k_cache, void* v_cache) {
   int b;
+  const int angles = rope_angles > 0 && rope_angles < D / 2 ? rope_angles : D / 2;
+  const double pscale = rope_scale > 0.0 ? rope_scale : 1.0;
   double *x = (double*)malloc(sizeof(double) * D), *y = (double*)malloc(sizeof(double) * D),
          *z = (double*)malloc(sizeof(double) * D);
   if (!x || !y || !z) {
@@ -210,15 +219,15 @@ int ref_kv_cache_write(int dtype, int Hq, int Hkv, int D, int bs, double rope_th
           int64_t base = (tok * Hq + h) * (int64_t)D;
           for (d = 0; d < D; ++d) x[d] = load_elem(q, dtype, base + d);
           ref_rms_norm(x, wq, D, rms_eps, y);
-          ref_rope(y, D, (double)t, rope_theta, z);
+          ref_rope(y, D, (double)t, rope_theta, angles, pscale, z);
           for (d = 0; d < D; ++d) store_elem(q, dtype, base + d, z[d]);
         }
       }
-      for (h = 0; h < Hkv; ++h) {
+      for (h = 0; k && h < Hkv; ++h) {
         int64_t base = (tok * Hkv + h) * (int64_t)D;
         for (d = 0; d < D; ++d) x[d] = load_elem(k, dtype, base + d);
         ref_rms_norm(x, wk, D, rms_eps, y);
-        ref_rope(y, D, (double)t, rope_theta, z);
+        ref_rope(y, D, (double)t, rope_theta, angles, pscale, z);
         for (d = 0; d < D; ++d)
           store_elem(k_cache, dtype, k_index(blk, off, h, d, Hkv, bs, D, dtype, t), z[d]);
         if (!k_eq_v) {

@@ -36,17 +36,21 @@ class LayerParams(ctypes.Structure):
                 ("block_size", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("softcap", ctypes.c_float),
                 ("k_eq_v", ctypes.c_int32), ("rope_theta", ctypes.c_float),
-                ("rms_eps", ctypes.c_float)]
+                ("rms_eps", ctypes.c_float), ("rope_angles", ctypes.c_int32),
+                ("rope_scale", ctypes.c_float)]
 
 
 def layer_params(dtype, num_q_heads: int, num_kv_heads: int, head_dim: int, window: int = 0,
                  scale: float = 1.0, softcap: float = 0.0, k_eq_v: bool = False,
                  rope_theta: float = 10000.0, rms_eps: float = 1e-6,
-                 block_size: int = BLOCK_SIZE) -> LayerParams:
-    """dtype: torch.float32 / torch.bfloat16, or "fp32" / "bf16"."""
+                 block_size: int = BLOCK_SIZE, rope_angles: int = 0,
+                 rope_scale: float = 0.0) -> LayerParams:
+    """dtype: torch.float32 / torch.bfloat16, or "fp32" / "bf16".  rope_angles: rotated
+    frequency pairs (0 = all); rope_scale: linear position divisor (0 = none)."""
     code = GA_BF16 if dtype in (torch.bfloat16, "bf16", GA_BF16) else GA_FP32
     return LayerParams(code, num_q_heads, num_kv_heads, head_dim, block_size, window, scale,
-                       softcap, int(bool(k_eq_v)), rope_theta, rms_eps)
+                       softcap, int(bool(k_eq_v)), rope_theta, rms_eps, rope_angles,
+                       rope_scale)
 
 
 _lib = None
@@ -112,17 +116,22 @@ def _elem(p: LayerParams):
 
 def kv_cache_write(p: LayerParams, q, k, v, q_norm_w, k_norm_w, v_norm_w, cu_seqlens,
                    context_lens, block_table, k_cache, v_cache, stream=None) -> None:
-    """ga_kv_cache_write: norm + RoPE of q (in place) and k, norm of v, scatter into pages."""
+    """ga_kv_cache_write: norm + RoPE of q (in place) and k, norm of v, scatter into pages.
+    k = v = None: q only (a layer reading another layer's cache; nothing is stored, and
+    block_table / k_cache / v_cache may be None)."""
     lib = load_library()
     et = _elem(p)
+    total = (k if k is not None else q).shape[0]
     st = lib.ga_kv_cache_write(
         ctypes.byref(p), _ptr(q, "q", et), _ptr(k, "k", et), _ptr(v, "v", et),
         _ptr(q_norm_w, "q_norm_w", torch.float32), _ptr(k_norm_w, "k_norm_w", torch.float32),
         _ptr(v_norm_w, "v_norm_w", torch.float32), _ptr(cu_seqlens, "cu_seqlens", torch.int32),
         _ptr(context_lens, "context_lens", torch.int32),
-        _ptr(block_table, "block_table", torch.int32), block_table.shape[1],
-        context_lens.shape[0], k.shape[0], _ptr(k_cache, "k_cache", et),
-        _ptr(v_cache, "v_cache", et), k_cache.shape[0], _stream(stream))
+        _ptr(block_table, "block_table", torch.int32),
+        0 if block_table is None else block_table.shape[1],
+        context_lens.shape[0], total, _ptr(k_cache, "k_cache", et),
+        _ptr(v_cache, "v_cache", et), 0 if k_cache is None else k_cache.shape[0],
+        _stream(stream))
     _raise_on(st)
 
 

@@ -60,6 +60,11 @@ ga_status check_params(const ga_layer_params* p) {
                 (double)p->rope_theta);
   if (!isfinite(p->rms_eps) || p->rms_eps < 0.f)
     return fail(GA_ERR_INVALID_ARG, "rms_eps %g must be finite and >= 0", (double)p->rms_eps);
+  if (p->rope_angles < 0 || p->rope_angles > p->head_dim / 2)
+    return fail(GA_ERR_INVALID_ARG, "rope_angles %d outside 0 .. head_dim/2", p->rope_angles);
+  if (!isfinite(p->rope_scale) || p->rope_scale < 0.f)
+    return fail(GA_ERR_INVALID_ARG, "rope_scale %g must be finite and >= 0",
+                (double)p->rope_scale);
   return GA_OK;
 }
 
@@ -133,16 +138,25 @@ ga_status ga_kv_cache_write(const ga_layer_params* p, void* q, const void* k, co
                             int64_t num_blocks, void* stream) {
   ga_status s = check_params(p);
   if (s != GA_OK) return s;
-  if ((s = check_table(max_blocks, num_blocks, batch)) != GA_OK) return s;
-  if ((s = check_caches(p, k_cache, v_cache)) != GA_OK) return s;
   if (total_tokens < 0) return fail(GA_ERR_INVALID_ARG, "total_tokens %d < 0", total_tokens);
-  if (!k) return fail(GA_ERR_INVALID_ARG, "k is NULL");
-  if (p->k_eq_v && v) return fail(GA_ERR_INVALID_ARG, "k_eq_v=1 but v is not NULL");
-  if (!p->k_eq_v && !v) return fail(GA_ERR_INVALID_ARG, "v is NULL (k_eq_v=0)");
-  if (p->k_eq_v && v_norm_w)
-    return fail(GA_ERR_INVALID_ARG, "k_eq_v=1 but v_norm_w is not NULL");
-  if (!cu_seqlens || !context_lens || !block_table)
-    return fail(GA_ERR_INVALID_ARG, "cu_seqlens, context_lens and block_table are required");
+  const bool q_only = k == nullptr;  // a layer reading another layer's cache
+  if (q_only) {
+    if (!q) return fail(GA_ERR_INVALID_ARG, "q and k are both NULL");
+    if (v || k_norm_w || v_norm_w)
+      return fail(GA_ERR_INVALID_ARG, "k is NULL (q-only write) but v or a k/v norm is given");
+    if (batch < 0) return fail(GA_ERR_INVALID_ARG, "batch %d < 0", batch);
+    if (!cu_seqlens || !context_lens)
+      return fail(GA_ERR_INVALID_ARG, "cu_seqlens and context_lens are required");
+  } else {
+    if ((s = check_table(max_blocks, num_blocks, batch)) != GA_OK) return s;
+    if ((s = check_caches(p, k_cache, v_cache)) != GA_OK) return s;
+    if (p->k_eq_v && v) return fail(GA_ERR_INVALID_ARG, "k_eq_v=1 but v is not NULL");
+    if (!p->k_eq_v && !v) return fail(GA_ERR_INVALID_ARG, "v is NULL (k_eq_v=0)");
+    if (p->k_eq_v && v_norm_w)
+      return fail(GA_ERR_INVALID_ARG, "k_eq_v=1 but v_norm_w is not NULL");
+    if (!cu_seqlens || !context_lens || !block_table)
+      return fail(GA_ERR_INVALID_ARG, "cu_seqlens, context_lens and block_table are required");
+  }
   if (batch == 0 || total_tokens == 0) return ok();
   ga::KvWriteLaunch a;
   a.dtype_bf16 = p->dtype == GA_BF16;
@@ -151,6 +165,8 @@ ga_status ga_kv_cache_write(const ga_layer_params* p, void* q, const void* k, co
   a.Hkv = p->num_kv_heads;
   a.k_eq_v = p->k_eq_v;
   a.rope_theta = p->rope_theta;
+  a.rope_angles = p->rope_angles == 0 ? p->head_dim / 2 : p->rope_angles;
+  a.rope_scale = p->rope_scale == 0.f ? 1.f : p->rope_scale;
   a.rms_eps = p->rms_eps;
   a.q = q;
   a.k = k;

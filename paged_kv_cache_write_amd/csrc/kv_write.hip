@@ -39,7 +39,9 @@ struct KvWriteArgs {
   int32_t max_blocks, batch, total_tokens;
   int32_t Hq, Hkv, nslots, has_q, k_eq_v;
   int32_t slots_per_wg, groups;  // head slots per workgroup; workgroups per token
-  double theta, eps;
+  double theta, eps, pos_scale;
+  int32_t rope_angles;
+  int32_t has_kv;  // 0: q only (a layer that reads another layer's cache)
 };
 
 template <typename T>
@@ -114,18 +116,27 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
   const int64_t n = (int64_t)a.cu[b + 1] - a.cu[b];
   const int64_t t = (int64_t)a.ctx[b] - n + (tok - a.cu[b]);
   const int64_t page = t >> 4;
-  if (t < 0 || page >= a.max_blocks) return;  // inconsistent metadata: write nothing
-  const int64_t blk = a.bt[(int64_t)b * a.max_blocks + page];
-  if (blk < 0 || blk >= a.num_blocks) return;  // (all three exits are workgroup-uniform)
+  if (t < 0) return;  // inconsistent metadata: write nothing
+  int64_t blk = 0;
+  if (a.has_kv) {
+    if (page >= a.max_blocks) return;
+    blk = a.bt[(int64_t)b * a.max_blocks + page];
+    if (blk < 0 || blk >= a.num_blocks) return;  // (all the exits are workgroup-uniform)
+  }
   const int64_t off = t & 15;
 
-  // rotation table of position t: omega_k = theta^(-2k/D), angle t * omega_k
+  // rotation table of position t ([KUNLUN] 挑战 5 proportional RoPE; [INFLM] follow-up list,
+  // linear scaling): omega_k = theta^(-2k/D) for k < rope_angles, 0 above; angle
+  // (t / pos_scale) * omega_k
   const bool rope = a.theta > 0.0;
   if (rope) {
+    const double tp = (double)t / a.pos_scale;
     for (int k = threadIdx.x; k < H; k += 256) {
-      const double omega = 1.0 / pow(a.theta, (2.0 * k) / (double)D);
-      double sn, cs;
-      sincos((double)t * omega, &sn, &cs);
+      double sn = 0.0, cs = 1.0;
+      if (k < a.rope_angles) {
+        const double omega = 1.0 / pow(a.theta, (2.0 * k) / (double)D);
+        sincos(tp * omega, &sn, &cs);
+      }
       cos_t[k] = cs;
       sin_t[k] = sn;
     }
@@ -234,8 +245,11 @@ hipError_t launch_kv_write(const KvWriteLaunch& L, hipStream_t s) {
   a.Hq = L.Hq; a.Hkv = L.Hkv;
   a.has_q = L.q != nullptr;
   a.k_eq_v = L.k_eq_v;
-  a.nslots = (a.has_q ? L.Hq : 0) + L.Hkv + (L.k_eq_v ? 0 : L.Hkv);
+  a.has_kv = L.k != nullptr;
+  a.nslots = (a.has_q ? L.Hq : 0) + (a.has_kv ? L.Hkv + (L.k_eq_v ? 0 : L.Hkv) : 0);
   a.theta = (double)L.rope_theta;
+  a.rope_angles = L.rope_angles;
+  a.pos_scale = (double)L.rope_scale;
   a.eps = (double)L.rms_eps;
   const bool bf = L.dtype_bf16;
   switch (L.D) {

@@ -13,6 +13,8 @@ struct KvWriteLaunch {
   bool dtype_bf16;
   int D, Hq, Hkv, k_eq_v;
   float rope_theta, rms_eps;
+  int rope_angles;   // rotated frequency pairs (1 .. D/2)
+  float rope_scale;  // position divisor (> 0)
   void* q;
   const void* k;
   const void* v;

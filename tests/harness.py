@@ -25,7 +25,8 @@ def dtype_code(spec):
 def params(spec) -> ga.LayerParams:
     return ga.layer_params(spec.dtype, spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
                            window=spec.window, scale=spec.scale, softcap=spec.softcap,
-                           k_eq_v=spec.k_eq_v, rope_theta=spec.rope_theta, rms_eps=spec.rms_eps)
+                           k_eq_v=spec.k_eq_v, rope_theta=spec.rope_theta, rms_eps=spec.rms_eps,
+                           rope_angles=spec.rope_angles, rope_scale=spec.rope_scale)
 
 
 def i32(a, device):
@@ -103,8 +104,10 @@ def oracle_write(spec, w_cpu, block_table, kc, vc, q, k, v, cu, cl):
     wq, wk, wv = (None if x is None else x.numpy() for x in w_cpu)
     oracle.kv_cache_write(dtype_code(spec), spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
                           float(np.float32(spec.rope_theta)), float(np.float32(spec.rms_eps)),
-                          int(spec.k_eq_v), qh, nb(k), None if v is None else nb(v), wq, wk, wv,
-                          cu, cl, block_table, kc, vc)
+                          int(spec.k_eq_v), qh, None if k is None else nb(k),
+                          None if v is None else nb(v), wq, wk, wv, cu, cl, block_table, kc, vc,
+                          rope_angles=spec.rope_angles,
+                          rope_scale=float(np.float32(spec.rope_scale)))
     return qh
 
 

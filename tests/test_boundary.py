@@ -87,6 +87,10 @@ INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 3
     (dict(scale=float("nan")), INVALID, "scale"),
     (dict(rope_theta=-1.0), INVALID, "rope_theta"),
     (dict(rms_eps=-1e-6), INVALID, "rms_eps"),
+    (dict(rope_angles=-1), INVALID, "rope_angles"),
+    (dict(rope_angles=129), INVALID, "rope_angles"),     # > head_dim / 2
+    (dict(rope_scale=-8.0), INVALID, "rope_scale"),
+    (dict(rope_scale=float("nan")), INVALID, "rope_scale"),
 ])
 def test_decode_rejects_bad_params(kw, code, msg):
     st, err = call_decode(good(**kw))
@@ -126,6 +130,14 @@ def test_write_rejects_bad_arguments():
     assert call_write(p, total=-1)[0] == INVALID
     assert call_write(p, num_blocks=0)[0] == INVALID
     assert call_write(good(softcap=-2.0))[0] == INVALID
+    # q-only write (a layer reading another layer's cache): k = v = None needs q, refuses
+    # k/v inputs and norms
+    assert call_write(p, k=None, v=FAKE)[0] == INVALID
+    assert call_write(p, k=None, v=None, q=None)[0] == INVALID
+    assert call_write(p, k=None, v=None, wk=FAKE)[0] == INVALID
+    assert call_write(p, k=None, v=None, wv=FAKE)[0] == INVALID
+    assert call_write(p, k=None, v=None, cl=None)[0] == INVALID
+    assert call_write(p, k=None, v=None, batch=-1)[0] == INVALID
 
 
 def test_prefill_rejects_bad_arguments():

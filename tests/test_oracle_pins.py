@@ -207,6 +207,65 @@ def test_rope_equals_complex_rotation_of_half_pairs():
                                atol=1e-11)
 
 
+def _pair_angles(D, theta, angles=0, pos_scale=1.0, t=1.0):
+    """Angle each pair (k, k + D/2) turns by, read back by rotating the unit vectors e_k."""
+    out = np.empty(D // 2)
+    for k in range(D // 2):
+        e = np.zeros(D)
+        e[k] = 1.0
+        y = oracle.rope(e, t, theta, angles, pos_scale)
+        out[k] = math.atan2(y[k + D // 2], y[k])
+        assert not np.delete(y, [k, k + D // 2]).any()
+    return out
+
+
+@pytest.mark.parametrize("D,theta,n", [(512, 1e6, 64), (256, 1e4, 32), (8, 10.0, 1)])
+def test_proportional_rope_listing_frequencies(D, theta, n):
+    """[KUNLUN] 挑战 5: with n rotated angles the exponent still divides by the head size (not
+    by 2n), and the D/2 - n remaining pairs get frequency 0 (identity).  Built here as the
+    page's list: base^(-(0, 2, .., 2n-2) / head_size) followed by zeros."""
+    listing = np.concatenate([1.0 / theta ** (np.arange(0, 2 * n, 2, dtype=np.float64) / D),
+                              np.zeros(D // 2 - n)])
+    np.testing.assert_allclose(_pair_angles(D, theta, n), listing, rtol=0, atol=1e-12)
+    # the plausible slip of normalising by the rotated width instead would differ
+    wrong = 1.0 / theta ** (np.arange(0, 2 * n, 2, dtype=np.float64) / (2 * n))
+    if n > 1:
+        assert np.abs(_pair_angles(D, theta, n)[:n] - wrong).max() > 1e-3
+
+
+def test_proportional_rope_special_cases():
+    rng = np.random.default_rng(41)
+    D, theta = 256, 1e4
+    x = rng.standard_normal(D)
+    full = oracle.rope(x, 777.0, theta)
+    np.testing.assert_array_equal(oracle.rope(x, 777.0, theta, D // 2), full)  # n = D/2: full
+    np.testing.assert_array_equal(oracle.rope(x, 777.0, theta, 0), full)       # 0 means all
+    y = oracle.rope(x, 777.0, theta, 16)
+    keep = np.r_[16:D // 2, D // 2 + 16:D]
+    np.testing.assert_array_equal(y[keep], x[keep])          # unrotated dims pass through
+    rot = np.r_[0:16, D // 2:D // 2 + 16]
+    np.testing.assert_array_equal(y[rot], full[rot])         # rotated dims as under full RoPE
+
+
+def test_linear_rope_scaling_divides_the_position():
+    """[INFLM] follow-up list: linear scaling divides the position by the factor, so position
+    f*m under factor f turns exactly like position m unscaled, and every pair's angle at one
+    position is the unscaled frequency over f."""
+    rng = np.random.default_rng(42)
+    D, theta, f = 512, 1e6, 8.0
+    x = rng.standard_normal(D)
+    for m in (0, 1, 5, 4099):
+        np.testing.assert_allclose(oracle.rope(x, f * m, theta, 0, f),
+                                   oracle.rope(x, float(m), theta), rtol=0, atol=1e-12)
+    listing = 1.0 / theta ** (np.arange(0, D, 2, dtype=np.float64) / D)
+    np.testing.assert_allclose(_pair_angles(D, theta, 0, f), listing / f, rtol=0, atol=1e-15)
+    # scaled rotations stay relative: the score depends on the distance only
+    z = rng.standard_normal(D)
+    a = oracle.rope(x, 900.0, theta, 0, f) @ oracle.rope(z, 13.0, theta, 0, f)
+    b = oracle.rope(x, 1887.0, theta, 0, f) @ oracle.rope(z, 1000.0, theta, 0, f)
+    assert abs(a - b) < 1e-9
+
+
 # ------------------------------------------------------------------ write path ------------
 
 def test_plain_scatter_is_bit_exact_both_dtypes():
@@ -295,6 +354,52 @@ def test_write_positions_follow_context_lens():
             row = page_rows(kc[bt[b, t // BS], 0].reshape(-1), D, unit_elems("fp32"),
                             (t // BS) % 2)[t % BS]
             assert abs(row[0] - math.cos(t)) < 1e-7 and abs(row[D // 2] - math.sin(t)) < 1e-7
+
+
+def test_write_proportional_scaled_rope_and_q_only_layer():
+    """Write with n rotated angles and a linear factor f ([KUNLUN] 挑战 5, [INFLM] follow-up
+    list), checked against torch's RMSNorm and the complex rotation with the page's frequency
+    list; then the same q through a layer that shares the cache ([KUNLUN] §4.3): k = v = None
+    normalises and rotates q identically and leaves both caches bit-for-bit unchanged."""
+    rng = np.random.default_rng(43)
+    Hq, Hkv, D, theta, eps, n, f = 4, 2, 16, 1e6, 1e-6, 2, 8.0
+    cl, cu = np.array([75], np.int32), np.array([0, 6], np.int32)
+    bt = np.array([[5, 0, 3, 1, 2]], np.int32)
+    q = rng.standard_normal((6, Hq, D)).astype(np.float32)
+    k = rng.standard_normal((6, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((6, Hkv, D)).astype(np.float32)
+    ws = [(1 + 0.1 * rng.standard_normal(D)).astype(np.float32) for _ in range(3)]
+    kc = np.zeros((6, Hkv, BS, D), np.float32)
+    vc = np.zeros((6, Hkv, D, BS), np.float32)
+    q_out = q.copy()
+    oracle.kv_cache_write(FP32, Hq, Hkv, D, theta, eps, 0, q_out, k, v, *ws, cu, cl, bt, kc, vc,
+                          rope_angles=n, rope_scale=f)
+    inv = np.concatenate([1.0 / theta ** (np.arange(0, 2 * n, 2, dtype=np.float64) / D),
+                          np.zeros(D // 2 - n)])
+
+    def norm(x, w):
+        return torch.nn.functional.rms_norm(torch.from_numpy(x.astype(np.float64)), (D,),
+                                            torch.from_numpy(w.astype(np.float64)), eps).numpy()
+
+    def rot(x, t):
+        z = (x[..., :D // 2] + 1j * x[..., D // 2:]) * np.exp(1j * (t / f) * inv)
+        return np.concatenate([z.real, z.imag], -1)
+
+    for i in range(6):
+        t = 69 + i
+        blk, off = bt[0, t // BS], t % BS
+        np.testing.assert_allclose(q_out[i], rot(norm(q[i], ws[0]), t), rtol=2e-7, atol=2e-7)
+        krow = np.stack([page_rows(kc[blk, g].reshape(-1), D, unit_elems("fp32"),
+                                   (t // BS) % 2)[off] for g in range(Hkv)])
+        np.testing.assert_allclose(krow, rot(norm(k[i], ws[1]), t), rtol=2e-7, atol=2e-7)
+
+    kc0, vc0 = kc.copy(), vc.copy()
+    q_shared = q.copy()
+    oracle.kv_cache_write(FP32, Hq, Hkv, D, theta, eps, 0, q_shared, None, None, ws[0], None,
+                          None, cu, cl, bt, kc, vc, rope_angles=n, rope_scale=f)
+    np.testing.assert_array_equal(q_shared, q_out)
+    np.testing.assert_array_equal(kc, kc0)
+    np.testing.assert_array_equal(vc, vc0)
 
 
 # ------------------------------------------------------------------ attention -------------

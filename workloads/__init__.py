@@ -35,6 +35,8 @@ class LayerSpec:
     k_eq_v: bool = False
     rope_theta: float = 10000.0
     rms_eps: float = 1e-6
+    rope_angles: int = 0       # rotated frequency pairs (0 = all D/2)
+    rope_scale: float = 0.0    # linear RoPE position divisor (0 = none)
     norm_q: bool = True
     norm_k: bool = True
     norm_v: bool = True
