@@ -85,7 +85,8 @@ def params(spec):
     return ga.layer_params(spec.dtype, spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
                            window=spec.window, scale=spec.scale, softcap=spec.softcap,
                            k_eq_v=spec.k_eq_v, rope_theta=spec.rope_theta, rms_eps=spec.rms_eps,
-                           rope_angles=spec.rope_angles, rope_scale=spec.rope_scale)
+                           rope_angles=spec.rope_angles, rope_scale=spec.rope_scale,
+                           page_ring=spec.page_ring)
 
 
 def i32(a, dev):

@@ -39,7 +39,18 @@
  *   k_cache: [num_blocks][num_kv_heads][16 * head_dim]  one key page per (block, kv head)
  *   v_cache: [num_blocks][num_kv_heads][head_dim][16]   value columns, the 16 keys contiguous
  *   Token position t of sequence b lives in block block_table[b][t / 16], row r = t % 16 of
- *   the page whose logical index in the sequence is lp = t / 16.
+ *   the page whose logical index in the sequence is lp = t / 16.  With page_ring = 1 (sliding
+ *   layers only) the table row is a ring instead: logical page lp lives in block
+ *   block_table[b][lp % max_blocks], so a sliding layer holds O(window) pages per sequence
+ *   whatever its length ([INFLM] Gemma-3 §3 keeps a windowed cache and reads only the keys
+ *   inside the window; follow-up 2 gives the key range a chunk needs, past - W + 1 onwards).
+ *   Pages wrap in place: writing position t reuses the block of position t - 16*max_blocks.
+ *   A ring row must therefore hold every page a call reads after its write: for decode
+ *   max_blocks >= floor((W - 1) / 16) + 2, for a prefill chunk of at most n new tokens
+ *   max_blocks >= floor((n + W - 2) / 16) + 3 (the window of the chunk's first query, the
+ *   chunk itself, and one page for the 32-key tile alignment of the prefill kernel).  The
+ *   attention calls refuse smaller rings; ga_kv_cache_write cannot know the chunk a later call
+ *   attends with, so sizing the ring is the caller's part there.
  *   A key page is kept in 16-byte units: unit (row r, x) holds elements x*U .. x*U+U-1 of key
  *   row r (U = 8 for bf16, 4 for fp32) at unit slot 16*x + (r + 4*(lp % 2)) % 16 of the page,
  *   i.e. the 16 rows of one unit column are contiguous (256 bytes) and pages of odd logical
@@ -97,6 +108,10 @@ typedef struct {
   float rope_scale;     /* linear RoPE scaling ([INFLM] follow-up list: Gemma-3 global layers use
                            a linear factor, e.g. 8): the angle uses t / rope_scale instead of t;
                            0 means 1; < 0 or non-finite invalid */
+  int32_t page_ring;    /* 0: block_table[b][lp] holds logical page lp.  1: the table row is a
+                           ring of max_blocks pages, lp -> column lp % max_blocks (sliding-window
+                           page recycling, see the layout notes above); needs window > 0 and
+                           context lengths below 2^30.  Other values invalid */
 } ga_layer_params;
 
 /* Norm + rotate + scatter the new tokens of a batch ([KUNLUN] §4.3 forward of a layer that
@@ -141,7 +156,8 @@ size_t ga_decode_workspace_bytes(const ga_layer_params* p, int32_t batch,
  *   block_table  DEVICE int32 [batch][max_blocks].
  *   context_lens DEVICE int32 [batch], each in 1 .. max_context_len (the current token counts).
  *   max_context_len  HOST bound on context_lens, used to size the launch; must satisfy
- *                max_context_len <= max_blocks * 16.
+ *                max_context_len <= max_blocks * 16 (page_ring = 1: max_context_len < 2^30,
+ *                and max_blocks >= floor((W - 1) / 16) + 2).
  *   out          DEVICE [batch][Hq][D] in the storage dtype.
  *   workspace    DEVICE scratch of at least ga_decode_workspace_bytes(p, batch,
  *                max_context_len) bytes, 256-byte aligned; contents need no initialisation
@@ -159,7 +175,9 @@ ga_status ga_attn_decode(const ga_layer_params* p, const void* q, const void* k_
  *   q            DEVICE [total_q][Hq][D], normalised and rotated.
  *   cu_seqlens_q DEVICE int32 [batch+1], cu_seqlens_q[batch] == total_q.
  *   context_lens DEVICE int32 [batch] = past_b + n_b.
- *   max_q_len    HOST bound on every n_b (sizes the launch); max_q_len <= max_blocks * 16.
+ *   max_q_len    HOST bound on every n_b (sizes the launch); max_q_len <= max_blocks * 16
+ *                (page_ring = 1: max_blocks >= floor((max_q_len + W - 2) / 16) + 3, and
+ *                context_lens below 2^30).
  *   out          DEVICE [total_q][Hq][D]. */
 ga_status ga_attn_prefill(const ga_layer_params* p, const void* q,
                           const int32_t* cu_seqlens_q, const void* k_cache,
@@ -171,10 +189,14 @@ ga_status ga_attn_prefill(const ga_layer_params* p, const void* q,
 /* Checks, on HOST copies, the metadata the kernels read from device memory:
  *   cu_seqlens (HOST int32 [batch+1], may be NULL meaning one new token per sequence):
  *     starts at 0, non-decreasing;
- *   context_lens (HOST int32 [batch]): n_b <= context_lens[b] <= max_blocks * 16, and >= 1
- *     when require_nonempty;
+ *   context_lens (HOST int32 [batch]): n_b <= context_lens[b] <= max_blocks * 16 (page_ring:
+ *     < 2^30), and >= 1 when require_nonempty;
  *   block_table (HOST int32 [batch][max_blocks]): every page a sequence uses holds a block id
- *     in [0, num_blocks), and no two written slots of the call coincide.
+ *     in [0, num_blocks), and no two written slots of the call coincide.  page_ring = 1: the
+ *     columns of the pages an attention call reads after the write (the window of the first
+ *     new query through the last page, from the 32-key tile start when cu_seqlens is given),
+ *     as many of them as the ring holds, hold ids in range; that the ring is long enough for
+ *     the attention call is checked by that call.
  * Returns GA_OK or GA_ERR_INVALID_ARG (reason in ga_last_error()). */
 ga_status ga_check_metadata_host(const ga_layer_params* p, const int32_t* cu_seqlens,
                                  const int32_t* context_lens, const int32_t* block_table,

@@ -49,7 +49,7 @@ def _load():
         lib.ref_bf16_to_double.restype = dbl
         lib.ref_bf16_to_double.argtypes = [ctypes.c_uint16]
         lib.ref_slot.restype = i64
-        lib.ref_slot.argtypes = [P, i32, i32, i64, i32, P, P]
+        lib.ref_slot.argtypes = [P, i32, ctypes.c_int, i32, i64, i32, P, P]
         lib.ref_rms_norm.restype = None
         lib.ref_rms_norm.argtypes = [P, P, ctypes.c_int, dbl, P]
         lib.ref_rope.restype = None
@@ -57,13 +57,14 @@ def _load():
         lib.ref_kv_cache_write.restype = ctypes.c_int
         lib.ref_kv_cache_write.argtypes = [ctypes.c_int] * 5 + [dbl, ctypes.c_int, dbl, dbl,
                                                                 ctypes.c_int] + [P] * 6 \
-            + [P, P, P, i32, i32, P, P]
+            + [P, P, P, i32, ctypes.c_int, i32, P, P]
         lib.ref_attention.restype = ctypes.c_int
         lib.ref_attention.argtypes = [ctypes.c_int] * 6 + [dbl, dbl, ctypes.c_int, P, P, P, P, P,
-                                                           i32, P, i32, i32, P, i32, P]
+                                                           i32, ctypes.c_int, P, i32, i32, P,
+                                                           i32, P]
         lib.ref_attn_decode.restype = ctypes.c_int
         lib.ref_attn_decode.argtypes = [ctypes.c_int] * 6 + [dbl, dbl, ctypes.c_int, P, P, P, P,
-                                                             i32, P, i32, P]
+                                                             i32, ctypes.c_int, P, i32, P]
         _lib = lib
     return _lib
 
@@ -100,12 +101,13 @@ def bf16_to_double(h: int) -> float:
     return float(_load().ref_bf16_to_double(int(h)))
 
 
-def slot(block_table: np.ndarray, req: int, pos: int, block_size: int):
-    """(slot, block id, row in block) of token position ``pos`` of request ``req``."""
+def slot(block_table: np.ndarray, req: int, pos: int, block_size: int, page_ring: bool = False):
+    """(slot, block id, row in block) of token position ``pos`` of request ``req``; page_ring:
+    the table row is a ring (logical page p in entry p mod row length)."""
     bt = _check(np.ascontiguousarray(block_table, dtype=np.int32), np.int32, "block_table")
     blk, off = ctypes.c_int64(), ctypes.c_int64()
-    s = _load().ref_slot(_p(bt), bt.shape[1], req, pos, block_size, ctypes.byref(blk),
-                         ctypes.byref(off))
+    s = _load().ref_slot(_p(bt), bt.shape[1], int(bool(page_ring)), req, pos, block_size,
+                         ctypes.byref(blk), ctypes.byref(off))
     return int(s), int(blk.value), int(off.value)
 
 
@@ -132,10 +134,11 @@ def rope(x: np.ndarray, t: float, theta: float, angles: int = 0, pos_scale: floa
 
 def kv_cache_write(dtype, Hq, Hkv, D, rope_theta, rms_eps, k_eq_v, q, k, v, wq, wk, wv,
                    cu_seqlens, context_lens, block_table, k_cache, v_cache, block_size=16,
-                   rope_angles=0, rope_scale=0.0):
+                   rope_angles=0, rope_scale=0.0, page_ring=False):
     """Norm + RoPE + scatter in double; updates q (if given), k_cache and v_cache in place.
     k = v = None: q only (a layer sharing another layer's cache); rope_angles: rotated
-    frequency pairs (0 = all); rope_scale: position divisor (0 = 1)."""
+    frequency pairs (0 = all); rope_scale: position divisor (0 = 1); page_ring: the table rows
+    are rings (logical page p in entry p mod row length)."""
     et = _elem(dtype)
     q = _check(q, et, "q")
     k = _check(k, et, "k")
@@ -151,13 +154,14 @@ def kv_cache_write(dtype, Hq, Hkv, D, rope_theta, rms_eps, k_eq_v, q, k, v, wq, 
                                     int(rope_angles), float(rope_scale),
                                     float(rms_eps), int(k_eq_v), _p(q), _p(k), _p(v), _p(wq),
                                     _p(wk), _p(wv), _p(cu), _p(cl), _p(bt), bt.shape[1],
-                                    cl.shape[0], _p(k_cache), _p(v_cache))
+                                    int(bool(page_ring)), cl.shape[0], _p(k_cache), _p(v_cache))
     if rc:
         raise MemoryError("oracle kv_cache_write failed")
 
 
 def attention(dtype, Hq, Hkv, D, window, scale, softcap, k_eq_v, q, cu_seqlens_q, k_cache,
-              v_cache, block_table, context_lens, rows=None, block_size=16) -> np.ndarray:
+              v_cache, block_table, context_lens, rows=None, block_size=16,
+              page_ring=False) -> np.ndarray:
     """Plain softmax attention of the packed queries q [T][Hq][D] over the paged cache.
 
     Returns float64 [T][Hq][D]; rows not listed in ``rows`` (when given) are left as NaN."""
@@ -173,7 +177,8 @@ def attention(dtype, Hq, Hkv, D, window, scale, softcap, k_eq_v, q, cu_seqlens_q
     r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
     rc = _load().ref_attention(dtype, Hq, Hkv, D, block_size, int(window), float(scale),
                                float(softcap), int(k_eq_v), _p(q), _p(cu), _p(k_cache),
-                               _p(v_cache), _p(bt), bt.shape[1], _p(cl), cl.shape[0], total_q,
+                               _p(v_cache), _p(bt), bt.shape[1], int(bool(page_ring)), _p(cl),
+                               cl.shape[0], total_q,
                                _p(r), 0 if r is None else r.shape[0], _p(out))
     if rc:
         raise MemoryError("oracle attention failed")
@@ -181,7 +186,7 @@ def attention(dtype, Hq, Hkv, D, window, scale, softcap, k_eq_v, q, cu_seqlens_q
 
 
 def attn_decode(dtype, Hq, Hkv, D, window, scale, softcap, k_eq_v, q, k_cache, v_cache,
-                block_table, context_lens, block_size=16) -> np.ndarray:
+                block_table, context_lens, block_size=16, page_ring=False) -> np.ndarray:
     """One query per sequence at position context_lens[b]-1; returns float64 [B][Hq][D]."""
     et = _elem(dtype)
     q = _check(q, et, "q")
@@ -193,7 +198,8 @@ def attn_decode(dtype, Hq, Hkv, D, window, scale, softcap, k_eq_v, q, k_cache, v
     out = np.empty((B, Hq, D), dtype=np.float64)
     rc = _load().ref_attn_decode(dtype, Hq, Hkv, D, block_size, int(window), float(scale),
                                  float(softcap), int(k_eq_v), _p(q), _p(k_cache), _p(v_cache),
-                                 _p(bt), bt.shape[1], _p(cl), B, _p(out))
+                                 _p(bt), bt.shape[1], int(bool(page_ring)), _p(cl), B,
+                                 _p(out))
     if rc:
         raise MemoryError("oracle decode failed")
     return out

@@ -122,10 +122,14 @@ static void store_elem(void* base, int dtype, int64_t i, double x) {
 /* ---------------------------------------------------------------- paging ----------- */
 
 /* [KUNLUN] §6.3: slot = block_table[req][pos / block_size] * block_size + pos % block_size.
- * Returns the slot; *blk and *off receive the page id and the row inside the page. */
-int64_t ref_slot(const int32_t* block_table, int32_t max_blocks, int32_t req, int64_t pos,
-                 int32_t block_size, int64_t* blk, int64_t* off) {
-  int64_t b = block_table[(int64_t)req * max_blocks + pos / block_size];
+ * ring != 0: the row is a ring of max_blocks entries and logical page pos / block_size sits in
+ * entry (pos / block_size) mod max_blocks (a sliding layer's windowed cache, [INFLM] Gemma-3
+ * §3, kept in pages).  Returns the slot; *blk and *off receive the page id and the row inside
+ * the page. */
+int64_t ref_slot(const int32_t* block_table, int32_t max_blocks, int ring, int32_t req,
+                 int64_t pos, int32_t block_size, int64_t* blk, int64_t* off) {
+  int64_t page = pos / block_size;
+  int64_t b = block_table[(int64_t)req * max_blocks + (ring ? page % max_blocks : page)];
   int64_t o = pos % block_size;
   if (blk) *blk = b;
   if (off) *off = o;
@@ -196,7 +200,8 @@ int ref_kv_cache_write(int dtype, int Hq, int Hkv, int D, int bs, double rope_th
                        const void* k, const void* v,
                        const float* wq, const float* wk, const float* wv,
                        const int32_t* cu_seqlens, const int32_t* context_lens,
-                       const int32_t* block_table, int32_t max_blocks, int32_t batch,
+                       const int32_t* block_table, int32_t max_blocks, int ring,
+                       int32_t batch,
                        void* k_cache, void* v_cache) {
   int b;
   const int angles = rope_angles > 0 && rope_angles < D / 2 ? rope_angles : D / 2;
@@ -213,7 +218,7 @@ int ref_kv_cache_write(int dtype, int Hq, int Hkv, int D, int bs, double rope_th
     int i, h, d;
     for (i = 0; i < n; ++i) {
       int64_t tok = cu_seqlens[b] + i, t = past + i, blk, off;
-      ref_slot(block_table, max_blocks, b, t, bs, &blk, &off);
+      ref_slot(block_table, max_blocks, ring, b, t, bs, &blk, &off);
       if (q) {
         for (h = 0; h < Hq; ++h) {
           int64_t base = (tok * Hq + h) * (int64_t)D;
@@ -246,13 +251,14 @@ int ref_kv_cache_write(int dtype, int Hq, int Hkv, int D, int bs, double rope_th
 
 /* Gather keys lo..hi of kv head g of sequence b into K[j-lo][d] and V[j-lo][d] (double). */
 static void gather(int dtype, int Hkv, int D, int bs, int k_eq_v, const void* k_cache,
-                   const void* v_cache, const int32_t* block_table, int32_t max_blocks, int b,
+                   const void* v_cache, const int32_t* block_table, int32_t max_blocks,
+                   int ring, int b,
                    int g, int64_t lo, int64_t hi, double* K, double* V) {
   int64_t j;
   int d;
   for (j = lo; j <= hi; ++j) {
     int64_t blk, off;
-    ref_slot(block_table, max_blocks, b, j, bs, &blk, &off);
+    ref_slot(block_table, max_blocks, ring, b, j, bs, &blk, &off);
     for (d = 0; d < D; ++d) {
       K[(j - lo) * D + d] = load_elem(k_cache, dtype, k_index(blk, off, g, d, Hkv, bs, D, dtype, j));
       V[(j - lo) * D + d] = k_eq_v ? K[(j - lo) * D + d]
@@ -291,13 +297,14 @@ static void attend(const double* qv, const double* K, const double* V, int64_t n
 int ref_attention(int dtype, int Hq, int Hkv, int D, int bs, int window, double scale,
                   double softcap, int k_eq_v, const void* q, const int32_t* cu_seqlens_q,
                   const void* k_cache, const void* v_cache, const int32_t* block_table,
-                  int32_t max_blocks, const int32_t* context_lens, int32_t batch,
+                  int32_t max_blocks, int ring, const int32_t* context_lens, int32_t batch,
                   int32_t total_q, const int32_t* rows, int32_t n_rows, double* out) {
   int G = Hq / Hkv, nr = rows ? n_rows : total_q, err = 0;
   int64_t maxlen = 0;
   int b, idx;
   for (b = 0; b < batch; ++b)
     if (context_lens[b] > maxlen) maxlen = context_lens[b];
+  if (window > 0 && window < maxlen) maxlen = window; /* keys one query can see */
 #pragma omp parallel
   {
     double *K = (double*)malloc(sizeof(double) * (size_t)(maxlen > 0 ? maxlen : 1) * D);
@@ -319,8 +326,8 @@ int ref_attention(int dtype, int Hq, int Hkv, int D, int bs, int window, double 
         for (h = 0; h < Hq; ++h) {
           int g = h / G;
           if (g != gcur) {
-            gather(dtype, Hkv, D, bs, k_eq_v, k_cache, v_cache, block_table, max_blocks, bb, g,
-                   lo, t, K, V);
+            gather(dtype, Hkv, D, bs, k_eq_v, k_cache, v_cache, block_table, max_blocks, ring,
+                   bb, g, lo, t, K, V);
             gcur = g;
           }
           for (d = 0; d < D; ++d) qv[d] = load_elem(q, dtype, ((int64_t)r * Hq + h) * D + d);
@@ -337,13 +344,14 @@ int ref_attention(int dtype, int Hq, int Hkv, int D, int bs, int window, double 
 int ref_attn_decode(int dtype, int Hq, int Hkv, int D, int bs, int window, double scale,
                     double softcap, int k_eq_v, const void* q, const void* k_cache,
                     const void* v_cache, const int32_t* block_table, int32_t max_blocks,
-                    const int32_t* context_lens, int32_t batch, double* out) {
+                    int ring, const int32_t* context_lens, int32_t batch, double* out) {
   int rc, b;
   int32_t* cu = (int32_t*)malloc(sizeof(int32_t) * (batch + 1));
   if (!cu) return 1;
   for (b = 0; b <= batch; ++b) cu[b] = b;
   rc = ref_attention(dtype, Hq, Hkv, D, bs, window, scale, softcap, k_eq_v, q, cu, k_cache,
-                     v_cache, block_table, max_blocks, context_lens, batch, batch, NULL, 0, out);
+                     v_cache, block_table, max_blocks, ring, context_lens, batch, batch, NULL, 0,
+                     out);
   free(cu);
   return rc;
 }

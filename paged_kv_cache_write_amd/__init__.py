@@ -37,20 +37,21 @@ class LayerParams(ctypes.Structure):
                 ("scale", ctypes.c_float), ("softcap", ctypes.c_float),
                 ("k_eq_v", ctypes.c_int32), ("rope_theta", ctypes.c_float),
                 ("rms_eps", ctypes.c_float), ("rope_angles", ctypes.c_int32),
-                ("rope_scale", ctypes.c_float)]
+                ("rope_scale", ctypes.c_float), ("page_ring", ctypes.c_int32)]
 
 
 def layer_params(dtype, num_q_heads: int, num_kv_heads: int, head_dim: int, window: int = 0,
                  scale: float = 1.0, softcap: float = 0.0, k_eq_v: bool = False,
                  rope_theta: float = 10000.0, rms_eps: float = 1e-6,
                  block_size: int = BLOCK_SIZE, rope_angles: int = 0,
-                 rope_scale: float = 0.0) -> LayerParams:
+                 rope_scale: float = 0.0, page_ring: bool = False) -> LayerParams:
     """dtype: torch.float32 / torch.bfloat16, or "fp32" / "bf16".  rope_angles: rotated
-    frequency pairs (0 = all); rope_scale: linear position divisor (0 = none)."""
+    frequency pairs (0 = all); rope_scale: linear position divisor (0 = none); page_ring: block
+    table rows are rings (logical page p in column p mod max_blocks; sliding layers only)."""
     code = GA_BF16 if dtype in (torch.bfloat16, "bf16", GA_BF16) else GA_FP32
     return LayerParams(code, num_q_heads, num_kv_heads, head_dim, block_size, window, scale,
                        softcap, int(bool(k_eq_v)), rope_theta, rms_eps, rope_angles,
-                       rope_scale)
+                       rope_scale, int(bool(page_ring)))
 
 
 _lib = None

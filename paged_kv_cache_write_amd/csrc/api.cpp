@@ -65,6 +65,10 @@ ga_status check_params(const ga_layer_params* p) {
   if (!isfinite(p->rope_scale) || p->rope_scale < 0.f)
     return fail(GA_ERR_INVALID_ARG, "rope_scale %g must be finite and >= 0",
                 (double)p->rope_scale);
+  if (p->page_ring != 0 && p->page_ring != 1)
+    return fail(GA_ERR_INVALID_ARG, "page_ring %d must be 0 or 1", p->page_ring);
+  if (p->page_ring && p->window <= 0)
+    return fail(GA_ERR_INVALID_ARG, "page_ring needs a sliding window (window > 0)");
   return GA_OK;
 }
 
@@ -99,6 +103,16 @@ ga_status from_hip(hipError_t e, const char* what) {
   return fail(GA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Pages a ring row must hold: decode reads the window of its query, [L - W, L) (at most
+// floor((W - 1) / 16) + 2 pages); a prefill chunk of n tokens reads from its first query's
+// window start, rounded down to a 32-key tile, to its last key (at most
+// floor((n + W - 2) / 16) + 3 pages).
+int64_t ring_pages_decode(int window) { return (window - 1) / kPage + 2; }
+int64_t ring_pages_prefill(int window, int64_t max_q_len) {
+  return (max_q_len + window - 2) / kPage + 3;
+}
+constexpr int64_t kRingMaxLen = int64_t(1) << 30;  // context lengths stay below this
+
 ga::AttnLaunch make_attn(const ga_layer_params* p) {
   ga::AttnLaunch a;
   memset(&a, 0, sizeof a);
@@ -107,6 +121,7 @@ ga::AttnLaunch make_attn(const ga_layer_params* p) {
   a.Hq = p->num_q_heads;
   a.Hkv = p->num_kv_heads;
   a.window = p->window;
+  a.ring = p->page_ring;
   a.k_eq_v = p->k_eq_v;
   a.scale = p->scale;
   a.softcap = p->softcap;
@@ -167,6 +182,7 @@ ga_status ga_kv_cache_write(const ga_layer_params* p, void* q, const void* k, co
   a.rope_theta = p->rope_theta;
   a.rope_angles = p->rope_angles == 0 ? p->head_dim / 2 : p->rope_angles;
   a.rope_scale = p->rope_scale == 0.f ? 1.f : p->rope_scale;
+  a.ring = p->page_ring;
   a.rms_eps = p->rms_eps;
   a.q = q;
   a.k = k;
@@ -207,11 +223,23 @@ ga_status ga_attn_decode(const ga_layer_params* p, const void* q, const void* k_
     return fail(GA_ERR_INVALID_ARG, "q, out, block_table and context_lens are required");
   if (max_context_len < 1)
     return fail(GA_ERR_INVALID_ARG, "max_context_len %d < 1", max_context_len);
-  if ((int64_t)max_context_len > (int64_t)max_blocks * kPage)
+  if (p->page_ring) {
+    if ((int64_t)max_context_len >= kRingMaxLen)
+      return fail(GA_ERR_INVALID_ARG, "max_context_len %d: a ring table needs lengths < 2^30",
+                  max_context_len);
+    if (max_blocks < ring_pages_decode(p->window))
+      return fail(GA_ERR_INVALID_ARG, "ring of %d pages is shorter than the %lld a window of %d "
+                  "needs", max_blocks, (long long)ring_pages_decode(p->window), p->window);
+  } else if ((int64_t)max_context_len > (int64_t)max_blocks * kPage) {
     return fail(GA_ERR_INVALID_ARG, "max_context_len %d exceeds max_blocks*16 = %lld",
                 max_context_len, (long long)max_blocks * kPage);
-  if ((int64_t)batch * ((max_context_len + kPage - 1) / kPage) > 0x7fffffffLL)
-    return fail(GA_ERR_UNSUPPORTED, "batch x pages per sequence exceeds 2^31");
+  }
+  {
+    int64_t pages = (max_context_len + kPage - 1) / kPage;  // visible pages per sequence
+    if (p->window > 0 && pages > p->window / kPage + 2) pages = p->window / kPage + 2;
+    if ((int64_t)batch * pages > 0x7fffffffLL)
+      return fail(GA_ERR_UNSUPPORTED, "batch x visible pages per sequence exceeds 2^31");
+  }
   const ga::DecodePlan plan = ga::plan_decode(p->head_dim, p->num_q_heads, p->num_kv_heads,
                                               p->window, batch, max_context_len,
                                               p->dtype == GA_BF16);
@@ -257,6 +285,10 @@ ga_status ga_attn_prefill(const ga_layer_params* p, const void* q,
   if (max_q_len < 0) return fail(GA_ERR_INVALID_ARG, "max_q_len %d < 0", max_q_len);
   if ((int64_t)max_q_len > (int64_t)max_blocks * kPage)
     return fail(GA_ERR_INVALID_ARG, "max_q_len %d exceeds max_blocks*16", max_q_len);
+  if (p->page_ring && max_blocks < ring_pages_prefill(p->window, max_q_len))
+    return fail(GA_ERR_INVALID_ARG, "ring of %d pages is shorter than the %lld a chunk of %d "
+                "with a window of %d needs", max_blocks,
+                (long long)ring_pages_prefill(p->window, max_q_len), max_q_len, p->window);
   if (batch == 0 || total_q == 0 || max_q_len == 0) return ok();
   ga::AttnLaunch a = make_attn(p);
   a.q = q;
@@ -270,7 +302,7 @@ ga_status ga_attn_prefill(const ga_layer_params* p, const void* q,
   a.batch = batch;
   a.total_q = total_q;
   a.max_q_len = max_q_len;
-  a.max_context_len = max_blocks * kPage;
+  a.max_context_len = p->page_ring ? (int32_t)(kRingMaxLen - 1) : max_blocks * kPage;
   a.out = out;
   return from_hip(ga::launch_prefill(a, (hipStream_t)stream), "attn_prefill launch");
 }
@@ -296,19 +328,33 @@ ga_status ga_check_metadata_host(const ga_layer_params* p, const int32_t* cu_seq
                   (long long)L, (long long)n);
     if (require_nonempty && L < 1)
       return fail(GA_ERR_INVALID_ARG, "sequence %d: context_len %lld < 1", b, (long long)L);
-    if (L > (int64_t)max_blocks * kPage)
+    const int64_t pages = (L + kPage - 1) / kPage;
+    int64_t first = 0;  // first page whose block id must be valid
+    if (p->page_ring) {
+      if (L >= kRingMaxLen)
+        return fail(GA_ERR_INVALID_ARG, "sequence %d: context_len %lld >= 2^30 (ring table)", b,
+                    (long long)L);
+      // the pages an attention call reads after this write: from the window start of the
+      // first new query (prefill: from its 32-key tile) to the last page, as far as the ring
+      // holds them (whether it holds them all is checked by the attention calls)
+      const int64_t lo = L - n - p->window + 1 > 0 ? L - n - p->window + 1 : 0;
+      first = cu_seqlens ? 2 * (lo / (2 * kPage)) : lo / kPage;
+      if (pages - first > max_blocks) first = pages - max_blocks;
+    } else if (L > (int64_t)max_blocks * kPage) {
       return fail(GA_ERR_INVALID_ARG, "sequence %d: context_len %lld > max_blocks*16", b,
                   (long long)L);
-    const int64_t pages = (L + kPage - 1) / kPage;
-    for (int64_t pg = 0; pg < pages; ++pg) {
-      const int64_t blk = block_table[(int64_t)b * max_blocks + pg];
+    }
+    auto column = [&](int64_t pg) {
+      return (int64_t)b * max_blocks + (p->page_ring ? pg % max_blocks : pg);
+    };
+    for (int64_t pg = first; pg < pages; ++pg) {
+      const int64_t blk = block_table[column(pg)];
       if (blk < 0 || blk >= num_blocks)
         return fail(GA_ERR_INVALID_ARG, "sequence %d page %lld: block id %lld outside [0, %lld)",
                     b, (long long)pg, (long long)blk, (long long)num_blocks);
     }
     for (int64_t t = L - n; t < L; ++t)
-      written.push_back((int64_t)block_table[(int64_t)b * max_blocks + t / kPage] * kPage +
-                        t % kPage);
+      written.push_back((int64_t)block_table[column(t / kPage)] * kPage + t % kPage);
   }
   std::sort(written.begin(), written.end());
   if (std::adjacent_find(written.begin(), written.end()) != written.end())

@@ -21,7 +21,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* q, const int
                                                        const float* kc, const float* vc,
                                                        const int32_t* bt, const int32_t* ctx,
                                                        float* out, int64_t num_blocks,
-                                                       int max_blocks, int batch, int Hq,
+                                                       int max_blocks, int ring, int batch,
+                                                       int Hq,
                                                        int Hkv, int window, int k_eq_v,
                                                        int decode, int total_q, int max_len,
                                                        float scale, float cap) {
@@ -61,8 +62,9 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* q, const int
   float m = -INFINITY, l = 0.f;
   for (int key = lo; key <= t; ++key) {
     const int page = key / kPage;
-    if (page >= max_blocks) break;
-    const int64_t blk = clamp_blk(bt[(int64_t)b * max_blocks + page], num_blocks);
+    if (!ring && page >= max_blocks) break;
+    const int64_t blk =
+        clamp_blk(bt[(int64_t)b * max_blocks + bt_col(page, max_blocks, ring)], num_blocks);
     const int off = key - page * kPage;
     const float* kp = kc + (blk * Hkv + g) * kPage * D;  // K page (k_page_elem layout)
     float kv[C];
@@ -99,7 +101,7 @@ hipError_t launch_f32_t(const AttnLaunch& L, bool decode, hipStream_t s) {
   hipLaunchKernelGGL((attn_f32_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, s,
                      (const float*)L.q, L.cu_seqlens_q, (const float*)L.k_cache,
                      (const float*)L.v_cache, L.block_table, L.context_lens, (float*)L.out,
-                     L.num_blocks, L.max_blocks, L.batch, L.Hq, L.Hkv, L.window, L.k_eq_v,
+                     L.num_blocks, L.max_blocks, L.ring, L.batch, L.Hq, L.Hkv, L.window, L.k_eq_v,
                      decode ? 1 : 0, total_q, L.max_context_len, L.scale, L.softcap);
   return hipGetLastError();
 }
@@ -120,6 +122,7 @@ AttnArgs make_attn_args(const AttnLaunch& L) {
   a.out = (uint16_t*)L.out;
   a.num_blocks = L.num_blocks;
   a.max_blocks = L.max_blocks;
+  a.ring = L.ring;
   a.batch = L.batch;
   a.max_ctx = L.max_context_len;
   a.Hq = L.Hq;

@@ -106,6 +106,7 @@ struct AttnArgs {
   uint16_t* out;
   int64_t num_blocks;
   int32_t max_blocks, batch, max_ctx, Hq, Hkv, G, window;
+  int32_t ring;                // block-table rows are rings of max_blocks pages
   int32_t nworkers;            // decode
   int32_t max_q_len, total_q;  // prefill
   ScoreConsts sc;

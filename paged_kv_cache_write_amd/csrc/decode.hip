@@ -62,7 +62,9 @@ __device__ __forceinline__ void decode_piece(const AttnArgs& a, const bf16x8_t (
 
   auto load_ids = [&](int chunk) -> int {
     const int i = chunk * 64 + lane;
-    return i < np ? (int)clamp_blk(a.bt[bt_row + pbeg + i], a.num_blocks) : 0;
+    return i < np ? (int)clamp_blk(a.bt[bt_row + bt_col(pbeg + i, a.max_blocks, a.ring)],
+                                   a.num_blocks)
+                  : 0;
   };
   int ids = load_ids(0);
   int ids_next = np > 64 ? load_ids(1) : 0;

@@ -88,6 +88,14 @@ __device__ __forceinline__ int64_t k_page_elem(int r, int d, int64_t lp) {
   return (int64_t)(d / U) * (16 * U) + (int64_t)((r + 4 * (int)(lp & 1)) & 15) * U + (d % U);
 }
 
+// Block-table column of logical page lp: lp itself, or lp mod max_blocks when the table row is
+// a ring (sliding-window page recycling: a sliding layer keeps only the pages its window and
+// the current chunk need, and position t reuses the block of position t - 16 max_blocks).
+// The page's parity in the K layout above stays that of lp, not of its column.
+__device__ __forceinline__ int bt_col(int lp, int max_blocks, int ring) {
+  return ring ? (int)((unsigned)lp % (unsigned)max_blocks) : lp;
+}
+
 // ------------------------------------------------------------------------ MFMA --------------
 
 __device__ __forceinline__ float4_t mfma_16x16x32(const bf16x8_t& a, const bf16x8_t& b,

@@ -41,7 +41,8 @@ struct KvWriteArgs {
   int32_t slots_per_wg, groups;  // head slots per workgroup; workgroups per token
   double theta, eps, pos_scale;
   int32_t rope_angles;
-  int32_t has_kv;  // 0: q only (a layer that reads another layer's cache)
+  int32_t has_kv;
+  int32_t ring;  // block-table rows are rings of max_blocks pages  // 0: q only (a layer that reads another layer's cache)
 };
 
 template <typename T>
@@ -119,8 +120,8 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
   if (t < 0) return;  // inconsistent metadata: write nothing
   int64_t blk = 0;
   if (a.has_kv) {
-    if (page >= a.max_blocks) return;
-    blk = a.bt[(int64_t)b * a.max_blocks + page];
+    if (!a.ring && page >= a.max_blocks) return;
+    blk = a.bt[(int64_t)b * a.max_blocks + bt_col((int)page, a.max_blocks, a.ring)];
     if (blk < 0 || blk >= a.num_blocks) return;  // (all the exits are workgroup-uniform)
   }
   const int64_t off = t & 15;
@@ -246,6 +247,7 @@ hipError_t launch_kv_write(const KvWriteLaunch& L, hipStream_t s) {
   a.has_q = L.q != nullptr;
   a.k_eq_v = L.k_eq_v;
   a.has_kv = L.k != nullptr;
+  a.ring = L.ring;
   a.nslots = (a.has_q ? L.Hq : 0) + (a.has_kv ? L.Hkv + (L.k_eq_v ? 0 : L.Hkv) : 0);
   a.theta = (double)L.rope_theta;
   a.rope_angles = L.rope_angles;

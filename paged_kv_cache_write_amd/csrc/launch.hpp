@@ -23,6 +23,7 @@ struct KvWriteLaunch {
   const int32_t* context_lens;
   const int32_t* block_table;
   int32_t max_blocks, batch, total_tokens;
+  int ring;  // block-table rows are rings of max_blocks pages
   void* k_cache;
   void* v_cache;
   int64_t num_blocks;
@@ -40,6 +41,7 @@ struct AttnLaunch {
   int64_t num_blocks;
   const int32_t* block_table;
   int32_t max_blocks;
+  int ring;  // block-table rows are rings of max_blocks pages
   const int32_t* context_lens;
   int32_t batch;
   int32_t max_context_len;  // decode: host bound on context_lens

@@ -244,14 +244,19 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
     TileIds r{0, 0};
     if (tile < 0 || tile >= ntiles) return r;
     const int page = 2 * (kt0 + tile);  // <= last_page for every tile of the range
-    if (page + 1 <= last_page) {
+    if (page + 1 <= last_page && !a.ring) {
       const int2 v = scalar_load2(a.bt + bt_row + page);
       r.a = clamp_blk(v.x, a.num_blocks);
       r.b = clamp_blk(v.y, a.num_blocks);
+    } else if (page + 1 <= last_page) {  // ring row: the two columns need not be adjacent
+      r.a = clamp_blk(scalar_load1(a.bt + bt_row + bt_col(page, a.max_blocks, 1)), a.num_blocks);
+      r.b = clamp_blk(scalar_load1(a.bt + bt_row + bt_col(page + 1, a.max_blocks, 1)),
+                      a.num_blocks);
     } else {
       // the second page lies past the context: alias the first (its keys are masked and its
       // values zeroed) and read nothing past the sequence's last page
-      r.a = r.b = clamp_blk(scalar_load1(a.bt + bt_row + page), a.num_blocks);
+      r.a = r.b = clamp_blk(scalar_load1(a.bt + bt_row + bt_col(page, a.max_blocks, a.ring)),
+                            a.num_blocks);
     }
     return r;
   };

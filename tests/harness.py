@@ -26,7 +26,8 @@ def params(spec) -> ga.LayerParams:
     return ga.layer_params(spec.dtype, spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
                            window=spec.window, scale=spec.scale, softcap=spec.softcap,
                            k_eq_v=spec.k_eq_v, rope_theta=spec.rope_theta, rms_eps=spec.rms_eps,
-                           rope_angles=spec.rope_angles, rope_scale=spec.rope_scale)
+                           rope_angles=spec.rope_angles, rope_scale=spec.rope_scale,
+                           page_ring=spec.page_ring)
 
 
 def i32(a, device):
@@ -93,7 +94,7 @@ class PagedCase:
         return oracle.attention(dtype_code(s), s.num_q_heads, s.num_kv_heads, s.head_dim,
                                 s.window, float(np.float32(s.scale)), float(np.float32(s.softcap)),
                                 int(s.k_eq_v), wl.to_numpy_bits(q_dev), cu, kc, vc,
-                                self.pb.block_table, cl, rows=rows)
+                                self.pb.block_table, cl, rows=rows, page_ring=s.page_ring)
 
 
 def oracle_write(spec, w_cpu, block_table, kc, vc, q, k, v, cu, cl):
@@ -107,7 +108,7 @@ def oracle_write(spec, w_cpu, block_table, kc, vc, q, k, v, cu, cl):
                           int(spec.k_eq_v), qh, None if k is None else nb(k),
                           None if v is None else nb(v), wq, wk, wv, cu, cl, block_table, kc, vc,
                           rope_angles=spec.rope_angles,
-                          rope_scale=float(np.float32(spec.rope_scale)))
+                          rope_scale=float(np.float32(spec.rope_scale)), page_ring=spec.page_ring)
     return qh
 
 

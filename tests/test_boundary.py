@@ -91,6 +91,8 @@ INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 3
     (dict(rope_angles=129), INVALID, "rope_angles"),     # > head_dim / 2
     (dict(rope_scale=-8.0), INVALID, "rope_scale"),
     (dict(rope_scale=float("nan")), INVALID, "rope_scale"),
+    (dict(page_ring=2), INVALID, "page_ring"),
+    (dict(page_ring=True, window=0), INVALID, "sliding window"),
 ])
 def test_decode_rejects_bad_params(kw, code, msg):
     st, err = call_decode(good(**kw))
@@ -140,6 +142,21 @@ def test_write_rejects_bad_arguments():
     assert call_write(p, k=None, v=None, batch=-1)[0] == INVALID
 
 
+def test_ring_tables_are_sized_on_the_host():
+    """A ring row must hold the decode window (floor((W - 1) / 16) + 2 pages) or a prefill
+    chunk plus its first query's window (floor((n + W - 2) / 16) + 3); lengths stay below 2^30.
+    Smaller rings are refused before anything is enqueued."""
+    p = good(window=1024, page_ring=True)
+    st, err = call_decode(p, max_blocks=64, max_context_len=36000)
+    assert st == INVALID and "65" in err
+    st, err = call_decode(p, max_blocks=65, max_context_len=1 << 30)
+    assert st == INVALID and "2^30" in err
+    st, err = call_prefill(p, max_blocks=78, max_q_len=256)      # needs (256+1022)//16+3 = 82
+    assert st == INVALID and "82" in err
+    # without the ring, a context beyond max_blocks * 16 is refused as before
+    assert call_decode(good(window=1024), max_blocks=65, max_context_len=36000)[0] == INVALID
+
+
 def test_prefill_rejects_bad_arguments():
     p = good()
     assert call_prefill(p, cu=None)[0] == INVALID
@@ -186,6 +203,22 @@ def test_metadata_check_host():
     _meta([0, 16], [0, 16], bt, 6, require=False)
     with pytest.raises(ga.GAError, match="decreases"):
         _meta([40, 16], [8, -1], bt, 6)
+
+
+def test_metadata_check_host_ring_rows():
+    """Ring rows (page_ring): only the pages the call reads must hold valid ids and fit the
+    ring; positions may run past max_blocks * 16."""
+    p = good(window=20, page_ring=True)
+    # prefill chunk of 8 at L = 100: keys from 2 * ((100 - 8 - 19) // 32) = page 4 .. page 6
+    _meta([100], [8], [[0, 1, 2, 3]], 4, p=p)
+    with pytest.raises(ga.GAError, match="outside"):
+        _meta([100], [8], [[99, 1, 2, 3]], 4, p=p)          # page 4 -> column 0
+    # a chunk of 80 new tokens wraps onto itself in a ring of 4 pages (64 slots)
+    with pytest.raises(ga.GAError, match="same cache slot"):
+        _meta([100], [80], [[0, 1, 2, 3]], 4, p=p)
+    # decode rule (no cu_seqlens): the window [80, 100) spans pages 5 and 6 only
+    ga.check_metadata_host(p, None, torch.tensor([100], dtype=torch.int32),
+                           torch.tensor([[99, 1, 2, 99]], dtype=torch.int32), 4)
 
 
 def test_status_strings():

@@ -132,6 +132,74 @@ def test_slots_of_a_sequence_are_a_bijection_onto_its_pages():
         assert sorted(slots) == expect
 
 
+def test_ring_slot_worked_example():
+    """A ring row of 5 entries: logical page p sits in entry p mod 5, so position t and
+    t + 80 share a slot.  Expected values worked by hand from slot = id * 16 + t % 16."""
+    bt = np.array([[7, 3, 9, 1, 4]], np.int32)
+    for pos, blk_id, off in ((0, 7, 0), (79, 4, 15), (83, 7, 3), (115, 9, 3), (1000, 9, 8)):
+        s, blk, o = oracle.slot(bt, 0, pos, 16, page_ring=True)
+        assert (blk, o, s) == (blk_id, off, blk_id * 16 + off), pos
+    # any 5 consecutive pages occupy 5 distinct entries; the plain table reads column p
+    for p0 in range(0, 40):
+        assert sorted(oracle.slot(bt, 0, 16 * p, 16, True)[1] for p in range(p0, p0 + 5)) == \
+            sorted(bt[0].tolist())
+    assert oracle.slot(bt, 0, 70, 16)[1] == 4
+
+
+def _serve_chunks(ring, W, lens, chunk, rng, Hq=4, Hkv=2, D=16):
+    """Write every sequence chunk by chunk (oracle write) and attend each chunk right after its
+    write (oracle attention), once through a plain table and once through a ring table of
+    `ring` entries per sequence.  Returns the two lists of chunk outputs."""
+    B = len(lens)
+    pages = [-(-L // BS) for L in lens]
+    plain_bt = np.arange(sum(pages) + 0, dtype=np.int32)
+    bt_full = np.zeros((B, max(pages)), np.int32)
+    at = 0
+    for b in range(B):
+        bt_full[b, :pages[b]] = plain_bt[at:at + pages[b]]
+        at += pages[b]
+    bt_ring = rng.permutation(B * ring).astype(np.int32).reshape(B, ring)
+    caches = {}
+    for name, bt, nb in (("full", bt_full, sum(pages)), ("ring", bt_ring, B * ring)):
+        caches[name] = (np.full((nb, Hkv, BS, D), np.nan, np.float32),
+                        np.full((nb, Hkv, D, BS), np.nan, np.float32), bt)
+    outs = {"full": [], "ring": []}
+    done = np.zeros(B, np.int64)
+    while (done < lens).any():
+        n = np.minimum(np.asarray(lens) - done, chunk).astype(np.int32)
+        cl = (done + n).astype(np.int32)
+        cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+        T = int(cu[-1])
+        k = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+        v = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+        q = rng.standard_normal((T, Hq, D)).astype(np.float32)
+        for name in ("full", "ring"):
+            kc, vc, bt = caches[name]
+            oracle.kv_cache_write(FP32, Hq, Hkv, D, 1e4, 1e-6, 0, None, k, v, None, None, None,
+                                  cu, cl, bt, kc, vc, page_ring=(name == "ring"))
+            outs[name].append(oracle.attention(FP32, Hq, Hkv, D, W, 1.0, 0.0, 0, q, cu, kc, vc,
+                                               bt, cl, page_ring=(name == "ring")))
+        done += n
+    return outs["full"], outs["ring"]
+
+
+def test_ring_table_serves_the_window_exactly_like_a_plain_table():
+    """[INFLM] Gemma-3 §3 / follow-up 2: a sliding layer's chunk needs only keys from its first
+    query's window start on.  A ring of floor((n + W - 2) / 16) + 3 pages (the bound the
+    library enforces for prefill chunks of n) keeps all of them through every chunk's write,
+    so each chunk's attention equals the plain table's bit for bit; a ring of ceil(W / 16)
+    pages does not."""
+    rng = np.random.default_rng(60)
+    W, chunk, lens = 37, 20, [300, 45, 145]
+    ring = (chunk + W - 2) // BS + 3
+    full, ring_out = _serve_chunks(ring, W, lens, chunk, rng)
+    assert len(full) == 15
+    for a, b in zip(full, ring_out):
+        np.testing.assert_array_equal(a, b)
+    full, small = _serve_chunks(-(-W // BS), W, lens, chunk, np.random.default_rng(60))
+    assert any(not np.array_equal(a, b) for a, b in zip(full, small))
+
+
 # ------------------------------------------------------------------ RMSNorm ---------------
 
 def test_rms_norm_matches_torch_library_routine():

@@ -37,6 +37,7 @@ class LayerSpec:
     rms_eps: float = 1e-6
     rope_angles: int = 0       # rotated frequency pairs (0 = all D/2)
     rope_scale: float = 0.0    # linear RoPE position divisor (0 = none)
+    page_ring: bool = False    # block-table rows are rings of pages (sliding layers)
     norm_q: bool = True
     norm_k: bool = True
     norm_v: bool = True
@@ -104,6 +105,21 @@ def paged_batch(context_lens: Sequence[int], n_new: Sequence[int], seed: int,
             bt[b, nb:] = fill
     return PagedBatch(cl.astype(np.int32), nn.astype(np.int32), bt, num_blocks,
                       np.asarray(spare_ids, dtype=np.int32))
+
+
+def ring_batch(context_lens: Sequence[int], n_new: Sequence[int], ring: int, seed: int,
+               spare: int = 16) -> PagedBatch:
+    """Block table whose rows are rings of `ring` pages: each sequence owns `ring` distinct
+    blocks (random, interleaved across sequences), logical page p in column p mod ring."""
+    cl = np.asarray(context_lens, dtype=np.int64)
+    nn = np.asarray(n_new, dtype=np.int64)
+    assert cl.shape == nn.shape and (nn <= cl).all() and (nn >= 0).all() and ring >= 1
+    num_blocks = len(cl) * ring + spare
+    g = torch.Generator().manual_seed(2000 + seed)
+    perm = torch.randperm(num_blocks, generator=g).numpy()
+    bt = perm[:len(cl) * ring].reshape(len(cl), ring).astype(np.int32)
+    return PagedBatch(cl.astype(np.int32), nn.astype(np.int32), bt, num_blocks,
+                      np.asarray(perm[len(cl) * ring:], dtype=np.int32))
 
 
 def _gen(seed: int, device) -> torch.Generator:
