@@ -16,6 +16,7 @@ back-to-back calls between two HIP events on the launch stream.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -128,16 +129,28 @@ def prefill_flops(spec, lens, news):
 # ----------------------------------------------------------------------------- set-up ---------
 
 class DecodeBench:
-    """Caches for one decode workload, the past written by the library, `copies` copies."""
+    """Caches for one decode workload, the past written by the library, `copies` copies.
+    exact=True (a K=V workload): the exact K=V form instead, unrotated keys stored once with 64
+    rotated pairs (Gemma-4's proportional RoPE at head size 512) and a v_norm weight."""
 
-    def __init__(self, name, copies, dev, seed=0):
+    def __init__(self, name, copies, dev, seed=0, exact=False):
         specs, pb = wl.workload(name)
         self.name, self.spec, self.pb, self.dev = name, specs[0], pb, dev
         s = self.spec
-        self.p = params(s)
+        if exact:
+            ws = wl.norm_weights(dataclasses.replace(s, k_eq_v=False), seed)
+            self.w = [ws[0].to(dev), ws[1].to(dev), None]
+            self.spec = s = dataclasses.replace(s, k_eq_v=2, rope_angles=64)
+            self.kvw = (self.w[1], ws[2].to(dev))
+            self.p = ga.layer_params(s.dtype, s.num_q_heads, s.num_kv_heads, s.head_dim,
+                                     window=s.window, scale=s.scale, softcap=s.softcap, k_eq_v=2,
+                                     rope_theta=s.rope_theta, rms_eps=s.rms_eps,
+                                     rope_angles=s.rope_angles, kv_norm_w=self.kvw)
+        else:
+            self.p = params(s)
+            self.w = [None if x is None else x.to(dev) for x in wl.norm_weights(s, seed)]
         lens = pb.context_lens
         past = lens - 1
-        self.w = [None if x is None else x.to(dev) for x in wl.norm_weights(s, seed)]
         self.bt = i32(pb.block_table, dev)
         self.cl = i32(lens, dev)
         self.cu1 = i32(np.arange(pb.batch + 1), dev)
@@ -223,6 +236,40 @@ class PrefillBench:
         L = self.layers[li]
         ga.attn_prefill(L["p"], L["q"], self.cu, L["kc"], L["vc"], self.bt, self.cl, self.max_q,
                         out=L["out"])
+
+
+def prefill_global_kv_forms(pf: "PrefillBench", reps: int):
+    """The chunked-prefill workload's global layer (D 512, 32/4 heads) in its two K=V forms:
+    k_eq_v = 1 (the stored rotated keys serve as values) and exact K=V (unrotated keys stored
+    once, 64 rotated pairs, values scaled by w_v / w_k).  Returns {form: attention ms}."""
+    dev, pb = pf.dev, pf.pb
+    base = pf.specs[-1]
+    lens, news = pb.context_lens, pb.n_new
+    past = lens - news
+    cu_past = i32(np.concatenate([[0], np.cumsum(past)]), dev)
+    res = {}
+    for form in ("k_eq_v", "exact_k_eq_v"):
+        exact = form == "exact_k_eq_v"
+        s = dataclasses.replace(base, k_eq_v=2 if exact else True,
+                                rope_angles=64 if exact else 0)
+        ws = [x.to(dev) for x in wl.norm_weights(dataclasses.replace(s, k_eq_v=False), 70)]
+        p = ga.layer_params(s.dtype, s.num_q_heads, s.num_kv_heads, s.head_dim, window=s.window,
+                            scale=s.scale, softcap=s.softcap, k_eq_v=s.k_eq_v,
+                            rope_theta=s.rope_theta, rms_eps=s.rms_eps,
+                            rope_angles=s.rope_angles,
+                            kv_norm_w=(ws[1], ws[2]) if exact else None)
+        kc, _ = wl.empty_caches(s, pb.num_blocks, dev)
+        _, kp, _ = wl.raw_qkv(s, int(past.sum()), 71, device=dev)
+        ga.kv_cache_write(p, None, kp, None, None, ws[1], None, cu_past, i32(past, dev), pf.bt,
+                          kc, None)
+        q, k, _ = wl.raw_qkv(s, pb.total_new, 72, device=dev)
+        ga.kv_cache_write(p, q, k, None, ws[0], ws[1], None, pf.cu, pf.cl, pf.bt, kc, None)
+        out = torch.empty_like(q)
+        res[form] = time_calls(lambda i: ga.attn_prefill(p, q, pf.cu, kc, None, pf.bt, pf.cl,
+                                                         pf.max_q, out=out), 1, reps, 1)
+        del kc, kp, q, k, out
+        torch.cuda.empty_cache()
+    return res
 
 
 # ----------------------------------------------------------------------------- timing ---------
@@ -357,8 +404,12 @@ def main():
     del graphs
     if not args.no_extra:
         extra = {}
-        for name in ("sliding_decode_bf16", "kv_shared_decode_bf16"):
-            db = DecodeBench(name, 2 if name == "kv_shared_decode_bf16" else args.copies, dev)
+        for name in ("sliding_decode_bf16", "kv_shared_decode_bf16",
+                     "kv_shared_decode_bf16_exact"):
+            exact = name.endswith("_exact")
+            base = name[:-len("_exact")] if exact else name
+            db = DecodeBench(base, 2 if base == "kv_shared_decode_bf16" else args.copies, dev,
+                             exact=exact)
             n = len(db.kcs)
             gx = capture_steps([lambda c=c: (db.write(c), db.attend(c)) for c in range(n)])
             wall_x = time_graph_steps(gx, max(args.steps // 2, 5), max(args.warmup // 2, 2))
@@ -393,6 +444,14 @@ def main():
             "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
             "per_layer_attn_ms": [round(x, 4) for x in a_layers],
             "step_TFLOPs": round(pf.flops / (wall_p * 1e-3) / 1e12, 2)}
+        gflops = prefill_flops(pf.specs[-1], pf.pb.context_lens, pf.pb.n_new)
+        forms = prefill_global_kv_forms(pf, 3)
+        for form, ms in forms.items():
+            log(f"chunked_prefill global layer, {form}: {ms:.3f} ms -> "
+                f"{gflops / (ms * 1e-3) / 1e12:.1f} TFLOP/s")
+        extra["chunked_prefill_bf16"]["global_layer_kv_forms_ms"] = {
+            "separate_v": round(a_layers[-1], 4),
+            **{f: round(ms, 4) for f, ms in forms.items()}}
         result["extra"] = extra
         del gp, pf
         torch.cuda.empty_cache()

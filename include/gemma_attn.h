@@ -97,8 +97,13 @@ typedef struct {
                            for Gemma 2); must be finite */
   float softcap;        /* > 0: score <- softcap * tanh(score / softcap) after scaling and
                            before mask and softmax; 0: off; < 0 or non-finite: invalid */
-  int32_t k_eq_v;       /* 1: one cache (k_cache) serves as keys and values; v, v_cache and
-                           v_norm_w must then be NULL */
+  int32_t k_eq_v;       /* 0: separate K and V caches.  1: one cache (k_cache) of normalised,
+                           rotated keys serves as keys and values.  2: exact K=V ([MNN] §6.2:
+                           K is k_norm + RoPE of the shared projection, V its v_norm without
+                           RoPE): k_cache holds the normalised keys UNROTATED, the attention
+                           kernels rotate them for the scores and read them unrotated, scaled by
+                           kv_v_norm_w / kv_k_norm_w (below), as values.  With 1 or 2,
+                           v, v_cache and v_norm_w must be NULL */
   float rope_theta;     /* RoPE base (1e4 sliding, 1e6 global); 0: no rotation; < 0 invalid */
   float rms_eps;        /* RMSNorm epsilon, >= 0 (Gemma layers use 1e-6) */
   int32_t rope_angles;  /* rotated frequency pairs n ([KUNLUN] 挑战 5, proportional RoPE): pair k
@@ -112,6 +117,12 @@ typedef struct {
                            ring of max_blocks pages, lp -> column lp % max_blocks (sliding-window
                            page recycling, see the layout notes above); needs window > 0 and
                            context lengths below 2^30.  Other values invalid */
+  const float* kv_k_norm_w; /* k_eq_v = 2 only (NULL otherwise): DEVICE fp32 [head_dim], the
+                           layer's k_norm and v_norm weights.  The attention calls take value d of
+                           a key as its stored element d times kv_v_norm_w[d] / kv_k_norm_w[d];
+                           both NULL: factor 1 (neither norm has a weight).  Weights must be
+                           nonzero.  Exact mode supports rope_angles (effective) <= 64 */
+  const float* kv_v_norm_w;
 } ga_layer_params;
 
 /* Norm + rotate + scatter the new tokens of a batch ([KUNLUN] §4.3 forward of a layer that

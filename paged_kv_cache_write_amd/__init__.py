@@ -37,21 +37,34 @@ class LayerParams(ctypes.Structure):
                 ("scale", ctypes.c_float), ("softcap", ctypes.c_float),
                 ("k_eq_v", ctypes.c_int32), ("rope_theta", ctypes.c_float),
                 ("rms_eps", ctypes.c_float), ("rope_angles", ctypes.c_int32),
-                ("rope_scale", ctypes.c_float), ("page_ring", ctypes.c_int32)]
+                ("rope_scale", ctypes.c_float), ("page_ring", ctypes.c_int32),
+                ("kv_k_norm_w", ctypes.c_void_p), ("kv_v_norm_w", ctypes.c_void_p)]
 
 
 def layer_params(dtype, num_q_heads: int, num_kv_heads: int, head_dim: int, window: int = 0,
                  scale: float = 1.0, softcap: float = 0.0, k_eq_v: bool = False,
                  rope_theta: float = 10000.0, rms_eps: float = 1e-6,
                  block_size: int = BLOCK_SIZE, rope_angles: int = 0,
-                 rope_scale: float = 0.0, page_ring: bool = False) -> LayerParams:
-    """dtype: torch.float32 / torch.bfloat16, or "fp32" / "bf16".  rope_angles: rotated
-    frequency pairs (0 = all); rope_scale: linear position divisor (0 = none); page_ring: block
-    table rows are rings (logical page p in column p mod max_blocks; sliding layers only)."""
+                 rope_scale: float = 0.0, page_ring: bool = False,
+                 kv_norm_w=None) -> LayerParams:
+    """dtype: torch.float32 / torch.bfloat16, or "fp32" / "bf16".  k_eq_v: 0/False separate
+    K and V, 1/True one cache of rotated keys serves both, 2 exact K=V (unrotated keys stored
+    once; kv_norm_w = (k_norm weight, v_norm weight) as device fp32 tensors, kept alive by the
+    caller, or None when neither norm has a weight).  rope_angles: rotated frequency pairs
+    (0 = all); rope_scale: linear position divisor (0 = none); page_ring: block table rows are
+    rings (logical page p in column p mod max_blocks; sliding layers only)."""
     code = GA_BF16 if dtype in (torch.bfloat16, "bf16", GA_BF16) else GA_FP32
+    kw = kvw = None
+    if kv_norm_w is not None:
+        wk, wv = kv_norm_w
+        for w in (wk, wv):
+            if not (isinstance(w, torch.Tensor) and w.is_cuda and w.dtype == torch.float32
+                    and w.is_contiguous() and w.numel() == head_dim):
+                raise TypeError("kv_norm_w: expected two contiguous fp32 device tensors [D]")
+        kw, kvw = wk.data_ptr(), wv.data_ptr()
     return LayerParams(code, num_q_heads, num_kv_heads, head_dim, block_size, window, scale,
-                       softcap, int(bool(k_eq_v)), rope_theta, rms_eps, rope_angles,
-                       rope_scale, int(bool(page_ring)))
+                       softcap, int(k_eq_v), rope_theta, rms_eps, rope_angles,
+                       rope_scale, int(bool(page_ring)), kw, kvw)
 
 
 _lib = None

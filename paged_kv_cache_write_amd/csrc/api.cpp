@@ -34,6 +34,7 @@ ga_status ok() {
 
 constexpr int kPage = 16;
 constexpr int kMaxGroupBf16 = 16;  // query heads per kv head held by one MFMA column block
+constexpr int kMaxExactAngles = 64;  // pairs the attention kernels rotate in exact K=V mode
 
 ga_status check_params(const ga_layer_params* p) {
   if (!p) return fail(GA_ERR_INVALID_ARG, "params is NULL");
@@ -53,8 +54,8 @@ ga_status check_params(const ga_layer_params* p) {
   if (!isfinite(p->scale)) return fail(GA_ERR_INVALID_ARG, "scale is not finite");
   if (!isfinite(p->softcap) || p->softcap < 0.f)
     return fail(GA_ERR_INVALID_ARG, "softcap %g must be finite and >= 0", (double)p->softcap);
-  if (p->k_eq_v != 0 && p->k_eq_v != 1)
-    return fail(GA_ERR_INVALID_ARG, "k_eq_v must be 0 or 1");
+  if (p->k_eq_v < 0 || p->k_eq_v > 2)
+    return fail(GA_ERR_INVALID_ARG, "k_eq_v must be 0, 1 or 2");
   if (!isfinite(p->rope_theta) || p->rope_theta < 0.f)
     return fail(GA_ERR_INVALID_ARG, "rope_theta %g must be finite and >= 0",
                 (double)p->rope_theta);
@@ -65,6 +66,16 @@ ga_status check_params(const ga_layer_params* p) {
   if (!isfinite(p->rope_scale) || p->rope_scale < 0.f)
     return fail(GA_ERR_INVALID_ARG, "rope_scale %g must be finite and >= 0",
                 (double)p->rope_scale);
+  if (p->k_eq_v != 2 && (p->kv_k_norm_w || p->kv_v_norm_w))
+    return fail(GA_ERR_INVALID_ARG, "kv_k_norm_w / kv_v_norm_w are for k_eq_v = 2 only");
+  if (p->k_eq_v == 2 && (p->kv_k_norm_w == nullptr) != (p->kv_v_norm_w == nullptr))
+    return fail(GA_ERR_INVALID_ARG, "k_eq_v = 2 needs both kv_k_norm_w and kv_v_norm_w, or "
+                "neither (values are the stored keys times v_norm_w / k_norm_w)");
+  if (p->k_eq_v == 2 && p->rope_theta > 0.f &&
+      (p->rope_angles == 0 ? p->head_dim / 2 : p->rope_angles) > kMaxExactAngles)
+    return fail(GA_ERR_UNSUPPORTED, "k_eq_v = 2 rotates at most %d frequency pairs in the "
+                "attention kernels (rope_angles %d, head_dim %d)", kMaxExactAngles,
+                p->rope_angles, p->head_dim);
   if (p->page_ring != 0 && p->page_ring != 1)
     return fail(GA_ERR_INVALID_ARG, "page_ring %d must be 0 or 1", p->page_ring);
   if (p->page_ring && p->window <= 0)
@@ -93,7 +104,8 @@ ga_status check_table(int32_t max_blocks, int64_t num_blocks, int32_t batch) {
 
 ga_status check_caches(const ga_layer_params* p, const void* k_cache, const void* v_cache) {
   if (!k_cache) return fail(GA_ERR_INVALID_ARG, "k_cache is NULL");
-  if (p->k_eq_v && v_cache) return fail(GA_ERR_INVALID_ARG, "k_eq_v=1 but v_cache is not NULL");
+  if (p->k_eq_v && v_cache)
+    return fail(GA_ERR_INVALID_ARG, "k_eq_v=%d but v_cache is not NULL", p->k_eq_v);
   if (!p->k_eq_v && !v_cache) return fail(GA_ERR_INVALID_ARG, "v_cache is NULL (k_eq_v=0)");
   return GA_OK;
 }
@@ -123,6 +135,11 @@ ga::AttnLaunch make_attn(const ga_layer_params* p) {
   a.window = p->window;
   a.ring = p->page_ring;
   a.k_eq_v = p->k_eq_v;
+  a.rope_theta = p->rope_theta;
+  a.rope_angles = p->rope_angles == 0 ? p->head_dim / 2 : p->rope_angles;
+  a.rope_scale = p->rope_scale == 0.f ? 1.f : p->rope_scale;
+  a.kv_kw = p->kv_k_norm_w;
+  a.kv_vw = p->kv_v_norm_w;
   a.scale = p->scale;
   a.softcap = p->softcap;
   return a;
@@ -165,10 +182,11 @@ ga_status ga_kv_cache_write(const ga_layer_params* p, void* q, const void* k, co
   } else {
     if ((s = check_table(max_blocks, num_blocks, batch)) != GA_OK) return s;
     if ((s = check_caches(p, k_cache, v_cache)) != GA_OK) return s;
-    if (p->k_eq_v && v) return fail(GA_ERR_INVALID_ARG, "k_eq_v=1 but v is not NULL");
+    if (p->k_eq_v && v)
+      return fail(GA_ERR_INVALID_ARG, "k_eq_v=%d but v is not NULL", p->k_eq_v);
     if (!p->k_eq_v && !v) return fail(GA_ERR_INVALID_ARG, "v is NULL (k_eq_v=0)");
     if (p->k_eq_v && v_norm_w)
-      return fail(GA_ERR_INVALID_ARG, "k_eq_v=1 but v_norm_w is not NULL");
+      return fail(GA_ERR_INVALID_ARG, "k_eq_v=%d but v_norm_w is not NULL", p->k_eq_v);
     if (!cu_seqlens || !context_lens || !block_table)
       return fail(GA_ERR_INVALID_ARG, "cu_seqlens, context_lens and block_table are required");
   }

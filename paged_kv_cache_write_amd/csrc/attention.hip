@@ -25,7 +25,9 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* q, const int
                                                        int Hq,
                                                        int Hkv, int window, int k_eq_v,
                                                        int decode, int total_q, int max_len,
-                                                       float scale, float cap) {
+                                                       float scale, float cap, int rope_pairs,
+                                                       float rope_theta, float rope_scale,
+                                                       const float* kv_kw, const float* kv_vw) {
   constexpr int C = D / 64;
   const int lane = threadIdx.x & 63;
   const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -59,6 +61,19 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* q, const int
     qv[e] = q[((int64_t)rq * Hq + h) * D + lane * C + e];
     o[e] = 0.f;
   }
+  // exact K=V (k_eq_v = 2): stored keys are unrotated; pair k of this lane's dimensions
+  // (lanes 0-31 hold the first halves of the pairs, lanes 32-63 the second) turns by
+  // key * omega_k for the scores, in double
+  const bool exact = k_eq_v == 2;
+  const bool first_half = lane < 32;
+  double omega[C];
+#pragma unroll
+  for (int e = 0; e < C; ++e) {
+    const int k = (lane & 31) * C + e;
+    omega[e] = (exact && k < rope_pairs)
+                   ? pow((double)rope_theta, -2.0 * k / (double)D) / (double)rope_scale
+                   : 0.0;
+  }
   float m = -INFINITY, l = 0.f;
   for (int key = lo; key <= t; ++key) {
     const int page = key / kPage;
@@ -70,9 +85,22 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* q, const int
     float kv[C];
 #pragma unroll
     for (int e = 0; e < C; ++e) kv[e] = kp[k_page_elem<4>(off, lane * C + e, page)];
+    float ks[C];  // the key as the scores see it
+#pragma unroll
+    for (int e = 0; e < C; ++e) ks[e] = kv[e];
+    if (exact && rope_pairs > 0) {
+#pragma unroll
+      for (int e = 0; e < C; ++e) {
+        const float partner = __shfl_xor(kv[e], 32, kWave);
+        double sn, cs;
+        sincos((double)key * omega[e], &sn, &cs);
+        ks[e] = first_half ? (float)((double)kv[e] * cs - (double)partner * sn)
+                           : (float)((double)kv[e] * cs + (double)partner * sn);
+      }
+    }
     float part = 0.f;
 #pragma unroll
-    for (int e = 0; e < C; ++e) part = fmaf(qv[e], kv[e], part);
+    for (int e = 0; e < C; ++e) part = fmaf(qv[e], ks[e], part);
 #pragma unroll
     for (int msk = 32; msk >= 1; msk >>= 1) part += __shfl_xor(part, msk, kWave);
     float sc = part * scale;
@@ -89,7 +117,11 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* q, const int
     m = m_new;
   }
 #pragma unroll
-  for (int e = 0; e < C; ++e) dst[e] = o[e] / l;
+  for (int e = 0; e < C; ++e) {
+    float f = 1.f;  // exact K=V: values are the stored keys times w_v / w_k
+    if (kv_vw) f = kv_vw[lane * C + e] / kv_kw[lane * C + e];
+    dst[e] = o[e] / l * f;
+  }
 }
 
 template <int D>
@@ -102,7 +134,9 @@ hipError_t launch_f32_t(const AttnLaunch& L, bool decode, hipStream_t s) {
                      (const float*)L.q, L.cu_seqlens_q, (const float*)L.k_cache,
                      (const float*)L.v_cache, L.block_table, L.context_lens, (float*)L.out,
                      L.num_blocks, L.max_blocks, L.ring, L.batch, L.Hq, L.Hkv, L.window, L.k_eq_v,
-                     decode ? 1 : 0, total_q, L.max_context_len, L.scale, L.softcap);
+                     decode ? 1 : 0, total_q, L.max_context_len, L.scale, L.softcap,
+                     L.rope_theta > 0.f ? L.rope_angles : 0, L.rope_theta, L.rope_scale,
+                     L.kv_kw, L.kv_vw);
   return hipGetLastError();
 }
 
@@ -132,6 +166,12 @@ AttnArgs make_attn_args(const AttnLaunch& L) {
   a.nworkers = 0;
   a.max_q_len = L.max_q_len;
   a.total_q = L.total_q;
+  a.kv_mode = L.k_eq_v;
+  a.rope_pairs = (L.k_eq_v == 2 && L.rope_theta > 0.f) ? L.rope_angles : 0;
+  a.rho0 = 1.0 / (2.0 * M_PI * (double)L.rope_scale);
+  a.rho_step = a.rope_pairs > 0 ? pow((double)L.rope_theta, -2.0 / (double)L.D) : 1.0;
+  a.kv_kw = L.kv_kw;
+  a.kv_vw = L.kv_vw;
   if (L.softcap > 0.f) {
     a.sc.c_scale = 0.f;
     a.sc.inv_cap = L.scale / L.softcap;

@@ -77,9 +77,11 @@ __device__ __forceinline__ uint32_t keep2(bool a, bool b) {
 
 // Row stride (elements) of a wave's LDS page buffer in the K=V path: 16 bytes of padding
 // shift consecutive rows by 4 banks so the column-wise reads of 4 rows hit distinct banks.
+// One page [16 keys][D] per wave for the K=V value reads, rows padded so that the rows of
+// a transposing read (4 keys x 4 columns per 16 lanes) fall 32 bytes apart in the banks.
 template <int D>
 struct KeqvLds {
-  static constexpr int kStride = D + 8;
+  static constexpr int kStride = D + 16;
   static constexpr int kElems = kPage * kStride;  // per wave
 };
 
@@ -110,7 +112,72 @@ struct AttnArgs {
   int32_t nworkers;            // decode
   int32_t max_q_len, total_q;  // prefill
   ScoreConsts sc;
+  // Exact K=V (k_eq_v = 2, [MNN] §6.2): the cache holds normalised keys without RoPE.  Pair k
+  // (dimensions k and k + D/2, k < rope_pairs) of a key at position t turns, for the scores,
+  // by 2 pi t rho_k with rho_k = rho0 * rho_step^k revolutions per position (rho0 =
+  // 1 / (2 pi rope_scale), rho_step = theta^(-2/D)); values are the stored keys times
+  // kv_vw[d] / kv_kw[d] (factor 1 when both are null).
+  int32_t kv_mode;     // 0 separate V, 1 K=V, 2 exact K=V
+  int32_t rope_pairs;  // 0: no rotation
+  double rho0, rho_step;
+  const float* kv_kw;
+  const float* kv_vw;
 };
+
+// cos and sin of 2 pi rev, for a revolution count formed in double: reduced to [0, 1) in
+// double, then the hardware sine and cosine (whose argument is in revolutions).
+__device__ __forceinline__ void cos_sin_rev(double rev, float& c, float& s) {
+  const float fr = (float)__builtin_amdgcn_fract(rev);
+  s = __builtin_amdgcn_sinf(fr);
+  c = __builtin_amdgcn_cosf(fr);
+}
+
+// Exact K=V: rotate the 8 pairs of two bf16 units of one key, unit `a` holding dimensions
+// 8x .. 8x+7 (pairs k = 8x + e) and unit `b` their partners k + D/2, for a key at position t:
+// a <- a cos - b sin, b <- b cos + a sin.  Each rotated value y goes back as two bf16 terms,
+// hi = bf16(y) (into ua / ub) and lo = bf16(y - hi) (into la / lb): the matrix cores take both,
+// so the scores see the rotated key to about 16 bits instead of rounding it a second time.
+// rho_x = rho0 * rho_step^(8x).
+__device__ __forceinline__ void rope_units_exact(u32x4_t& ua, u32x4_t& ub, u32x4_t& la,
+                                                 u32x4_t& lb, int x, double rho_x,
+                                                 double rho_step, int rope_pairs, int64_t t) {
+  double rho = rho_x;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    float c[2], s[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = 8 * x + 2 * w + h;
+      if (k < rope_pairs) {
+        cos_sin_rev((double)t * rho, c[h], s[h]);
+      } else {
+        c[h] = 1.f;
+        s[h] = 0.f;
+      }
+      rho *= rho_step;
+    }
+    const float a0 = __uint_as_float(ua[w] << 16), a1 = __uint_as_float(ua[w] & 0xffff0000u);
+    const float b0 = __uint_as_float(ub[w] << 16), b1 = __uint_as_float(ub[w] & 0xffff0000u);
+    const float ya0 = a0 * c[0] - b0 * s[0], ya1 = a1 * c[1] - b1 * s[1];
+    const float yb0 = b0 * c[0] + a0 * s[0], yb1 = b1 * c[1] + a1 * s[1];
+    ua[w] = __builtin_bit_cast(uint32_t, cvt_bf16x2(ya0, ya1));
+    ub[w] = __builtin_bit_cast(uint32_t, cvt_bf16x2(yb0, yb1));
+    la[w] = __builtin_bit_cast(uint32_t, cvt_bf16x2(ya0 - __uint_as_float(ua[w] << 16),
+                                                    ya1 - __uint_as_float(ua[w] & 0xffff0000u)));
+    lb[w] = __builtin_bit_cast(uint32_t, cvt_bf16x2(yb0 - __uint_as_float(ub[w] << 16),
+                                                    yb1 - __uint_as_float(ub[w] & 0xffff0000u)));
+  }
+}
+
+// rho0 * rho_step^k in double (the frequency of pair k in revolutions per position).
+__device__ __forceinline__ double rope_rho(const double rho0, const double rho_step, int k) {
+  double r = rho0, p = rho_step;
+  for (int e = k; e > 0; e >>= 1) {  // exponentiation by squaring
+    if (e & 1) r *= p;
+    p *= p;
+  }
+  return r;
+}
 
 // Keys of sequence b that a decode query at position L-1 sees, and the pages holding them:
 // L = min(context_len, max_ctx); keys lo .. L-1; pages p0 .. p0 + npg - 1 ([INFLM] Gemma-3 §3:

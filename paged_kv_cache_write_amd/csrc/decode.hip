@@ -48,10 +48,15 @@ struct StepRegs {
 
 // One piece: kv head g of sequence b, pages [pbeg, pend) (absolute page indices), visible keys
 // [lo, L).  Accumulates into acc.
-template <int D, bool CAP, bool KEQV>
+// EXACT (with KEQV): the stored keys are unrotated; the lane's two units of each of the first
+// two chunks (dimensions < 64, the ones exact mode may rotate) and their partners D/2 further
+// are rotated for QK^T (rho_x: the frequencies of their first pairs), while the values are
+// read unrotated.
+template <int D, bool CAP, bool KEQV, bool EXACT>
 __device__ __forceinline__ void decode_piece(const AttnArgs& a, const bf16x8_t (&qf)[D / 32],
                                              Acc<D>& acc, int b, int g, int L, int lo,
-                                             int pbeg, int pend, uint16_t* lds) {
+                                             int pbeg, int pend, uint16_t* lds,
+                                             const double (&rho_x)[2]) {
   using R = StepRegs<D, KEQV>;
   constexpr int NP = R::NP, NC = D / 32, ND = D / 16;
   const int lane = threadIdx.x & 63, c16 = lane & 15, j = lane >> 4;
@@ -119,13 +124,45 @@ __device__ __forceinline__ void decode_piece(const AttnArgs& a, const bf16x8_t (
     const int pg0 = pbeg + s * NP;              // first page of the step
     const int k0 = pg0 * kPage;
     const bool full = (s + 1) * NP <= np && k0 >= lo && k0 + NP * kPage <= L;
+    // exact K=V: the rotated copies of the rope units of this lane's key (row c16), as
+    // hi + lo bf16 terms
+    u32x4_t kr[2][2], kl[2][2];
+    if constexpr (EXACT) {
+      static_assert(KEQV && NP == 1, "exact K=V reads one page per step");
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        kr[c][0] = r.k[0][c];
+        kr[c][1] = r.k[0][c + NC / 2];
+        kl[c][0] = kl[c][1] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+      if (a.rope_pairs > 0) {
+        const int64_t t = (int64_t)pg0 * kPage + c16;
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          rope_units_exact(kr[c][0], kr[c][1], kl[c][0], kl[c][1], 4 * c + j, rho_x[c],
+                           a.rho_step, a.rope_pairs, t);
+      }
+    }
     // S^T = K Q^T for each page of the step
     float4_t sc[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       sc[p] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < NC; ++c) sc[p] = mfma_16x16x32(as_bf16x8(r.k[p][c]), qf[c], sc[p]);
+      for (int c = 0; c < NC; ++c) {
+        u32x4_t kop = r.k[p][c];
+        if constexpr (EXACT) {
+          if (c < 2) {
+            kop = kr[c][0];
+            sc[p] = mfma_16x16x32(as_bf16x8(kl[c][0]), qf[c], sc[p]);
+          }
+          if (c >= NC / 2 && c < NC / 2 + 2) {
+            kop = kr[c - NC / 2][1];
+            sc[p] = mfma_16x16x32(as_bf16x8(kl[c - NC / 2][1]), qf[c], sc[p]);
+          }
+        }
+        sc[p] = mfma_16x16x32(as_bf16x8(kop), qf[c], sc[p]);
+      }
     }
     if constexpr (KEQV) {
       // the page goes to this wave's LDS buffer for the transposed value reads
@@ -188,18 +225,17 @@ __device__ __forceinline__ void decode_piece(const AttnArgs& a, const bf16x8_t (
       constexpr int S = KeqvLds<D>::kStride;
       const short4_t pf = as_short4(u32x2_t{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])});
       wave_lds_sync();
-      const uint16_t* col = lds + (4 * j) * S + c16;
+      // V^T fragment (d = 16 n + c16, keys 4j .. 4j+3) by one transposing read: lane 4e + q
+      // of a group points at dimensions 16 n + 4q .. + 3 of key 4j + e
+      const uint16_t* col = lds + (4 * j + (c16 >> 2)) * S + 4 * (c16 & 3);
+      const uint32_t m01 = keep2(vk[0], vk[1]), m23 = keep2(vk[2], vk[3]);
 #pragma unroll
       for (int n = 0; n < ND; ++n) {
-        uint16_t e0 = col[0 * S + 16 * n], e1 = col[1 * S + 16 * n];
-        uint16_t e2 = col[2 * S + 16 * n], e3 = col[3 * S + 16 * n];
+        u32x2_t av = lds_read_tr16(col + 16 * n);
         if (!full) {
-          e0 = vk[0] ? e0 : (uint16_t)0;
-          e1 = vk[1] ? e1 : (uint16_t)0;
-          e2 = vk[2] ? e2 : (uint16_t)0;
-          e3 = vk[3] ? e3 : (uint16_t)0;
+          av.x &= m01;
+          av.y &= m23;
         }
-        const u32x2_t av = {(uint32_t)e0 | ((uint32_t)e1 << 16), (uint32_t)e2 | ((uint32_t)e3 << 16)};
         acc.o[n] = mfma_16x16x16(as_short4(av), pf, acc.o[n]);
       }
       wave_lds_sync();
@@ -207,7 +243,7 @@ __device__ __forceinline__ void decode_piece(const AttnArgs& a, const bf16x8_t (
   }
 }
 
-template <int D, bool CAP, bool KEQV>
+template <int D, bool CAP, bool KEQV, bool EXACT>
 __global__ __launch_bounds__(256) void decode_stream_kernel(AttnArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   const int lane = threadIdx.x & 63, c16 = lane & 15, j = lane >> 4;
@@ -253,6 +289,11 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(AttnArgs a) {
     pref += __builtin_amdgcn_readlane(incl, 63);
   }
 
+  double rho_x[2] = {0.0, 0.0};  // exact K=V: frequencies of pairs 8(4c + j), c = 0, 1
+  if constexpr (EXACT) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) rho_x[c] = rope_rho(a.rho0, a.rho_step, 8 * (4 * c + j));
+  }
   bf16x8_t qf[D / 32];
   int64_t u = u0;
   while (u < u1 && b < B) {
@@ -274,7 +315,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(AttnArgs a) {
     load_q<D>(qf, a.q + ((int64_t)b * a.Hq + g * G + (head_ok ? c16 : 0)) * D, head_ok);
     Acc<D> acc;
     acc.init();
-    decode_piece<D, CAP, KEQV>(a, qf, acc, b, g, L, lo, p0 + lp, p0 + lp + cnt, lds);
+    decode_piece<D, CAP, KEQV, EXACT>(a, qf, acc, b, g, L, lo, p0 + lp, p0 + lp + cnt, lds,
+                                      rho_x);
     acc.l += __shfl_xor(acc.l, 16, kWave);
     acc.l += __shfl_xor(acc.l, 32, kWave);
     const int64_t row = ((int64_t)worker + (int64_t)b * Hkv + g) * G + c16;
@@ -352,15 +394,20 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
   if (gi == 0) {
 #pragma unroll
     for (int g2 = 1; g2 < NG; ++g2) acc += part[g2 * C4 + c];
-    *(u32x2_t*)(dst + 4 * c) = u32x2_t{pack_bf16x2(acc[0] * inv, acc[1] * inv),
-                                       pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+    float4_t f = {inv, inv, inv, inv};
+    if (a.kv_vw) {  // exact K=V: values are the stored keys times w_v / w_k
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f[i] *= a.kv_vw[4 * c + i] / a.kv_kw[4 * c + i];
+    }
+    *(u32x2_t*)(dst + 4 * c) = u32x2_t{pack_bf16x2(acc[0] * f[0], acc[1] * f[1]),
+                                       pack_bf16x2(acc[2] * f[2], acc[3] * f[3])};
   }
 }
 
 // Resident single-wave workers the device can hold for one kernel variant: CUs x 4 SIMDs x
 // waves per SIMD (from the occupancy of 4-wave workgroups).  The answer depends only on the
 // device and the kernel, so it is computed once per (device, variant) and cached.
-template <int D, bool CAP, bool KEQV>
+template <int D, bool CAP, bool KEQV, bool EXACT>
 int resident_workers(size_t lds) {
   constexpr int kMaxDevices = 64;
   static std::atomic<int> cache[kMaxDevices];
@@ -373,7 +420,7 @@ int resident_workers(size_t lds) {
   int cus = 256, blocks = 1;
   if (dev >= 0) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &blocks, reinterpret_cast<const void*>(&decode_stream_kernel<D, CAP, KEQV>), 256,
+          &blocks, reinterpret_cast<const void*>(&decode_stream_kernel<D, CAP, KEQV, EXACT>), 256,
           lds) != hipSuccess || blocks < 1)
     blocks = 1;
   int w = cus * blocks * 4;
@@ -382,12 +429,12 @@ int resident_workers(size_t lds) {
   return w;
 }
 
-template <int D, bool CAP, bool KEQV>
+template <int D, bool CAP, bool KEQV, bool EXACT>
 hipError_t launch_t(AttnArgs a, int max_workers, hipStream_t s) {
   const size_t lds = KEQV ? (size_t)4 * KeqvLds<D>::kElems * sizeof(uint16_t) : 0;
-  const int res = resident_workers<D, CAP, KEQV>(lds);
+  const int res = resident_workers<D, CAP, KEQV, EXACT>(lds);
   a.nworkers = res < max_workers ? res : max_workers;
-  hipLaunchKernelGGL((decode_stream_kernel<D, CAP, KEQV>), dim3((a.nworkers + 3) / 4),
+  hipLaunchKernelGGL((decode_stream_kernel<D, CAP, KEQV, EXACT>), dim3((a.nworkers + 3) / 4),
                      dim3(256), lds, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -395,10 +442,19 @@ hipError_t launch_t(AttnArgs a, int max_workers, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D, bool CAP>
+hipError_t by_kv(const AttnArgs& a, int mw, int kv_mode, hipStream_t s) {
+  switch (kv_mode) {
+    case 0: return launch_t<D, CAP, false, false>(a, mw, s);
+    case 1: return launch_t<D, CAP, true, false>(a, mw, s);
+    case 2: return launch_t<D, CAP, true, true>(a, mw, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <int D>
-hipError_t by_flags(const AttnArgs& a, int mw, bool cap, bool keqv, hipStream_t s) {
-  if (cap) return keqv ? launch_t<D, true, true>(a, mw, s) : launch_t<D, true, false>(a, mw, s);
-  return keqv ? launch_t<D, false, true>(a, mw, s) : launch_t<D, false, false>(a, mw, s);
+hipError_t by_flags(const AttnArgs& a, int mw, bool cap, int kv_mode, hipStream_t s) {
+  return cap ? by_kv<D, true>(a, mw, kv_mode, s) : by_kv<D, false>(a, mw, kv_mode, s);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -437,11 +493,11 @@ hipError_t launch_decode(const AttnLaunch& L, const DecodePlan& plan, hipStream_
   a.ws_pref = (int32_t*)ws;
   a.ws_ml = (float*)(ws + plan.pref_bytes);
   a.ws_o = (float*)(ws + plan.pref_bytes + plan.ml_bytes);
-  const bool cap = L.softcap > 0.f, keqv = L.k_eq_v != 0;
+  const bool cap = L.softcap > 0.f;
   switch (L.D) {
-    case 128: return by_flags<128>(a, plan.nworkers, cap, keqv, s);
-    case 256: return by_flags<256>(a, plan.nworkers, cap, keqv, s);
-    case 512: return by_flags<512>(a, plan.nworkers, cap, keqv, s);
+    case 128: return by_flags<128>(a, plan.nworkers, cap, L.k_eq_v, s);
+    case 256: return by_flags<256>(a, plan.nworkers, cap, L.k_eq_v, s);
+    case 512: return by_flags<512>(a, plan.nworkers, cap, L.k_eq_v, s);
   }
   return hipErrorInvalidValue;
 }

@@ -111,6 +111,20 @@ __device__ __forceinline__ float4_t mfma_16x16x16(const short4_t& a, const short
 __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i receives,
+// as its element e (0..3), element i % 4 of the four 16-bit elements at the address given by
+// lane 4e + i / 4 of the group: if lane 4e + q points at four consecutive columns 4q .. 4q+3
+// of row e of a row-major block, lane i gets column i of rows 0..3, the layout of a
+// matrix-core operand whose reduction index runs over those rows.  (Layout measured on gfx950
+// with an in-bounds probe.)  `lds_byte` is an LDS byte address, 8-byte aligned.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const void* lds_byte) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const v4i16 v =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(
+          (void*)lds_byte));
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
 __device__ __forceinline__ short4_t as_short4(const u32x2_t& v) {
   return __builtin_bit_cast(short4_t, v);
 }

@@ -41,8 +41,8 @@ struct KvWriteArgs {
   int32_t slots_per_wg, groups;  // head slots per workgroup; workgroups per token
   double theta, eps, pos_scale;
   int32_t rope_angles;
-  int32_t has_kv;
-  int32_t ring;  // block-table rows are rings of max_blocks pages  // 0: q only (a layer that reads another layer's cache)
+  int32_t has_kv;  // 0: q only (a layer that reads another layer's cache)
+  int32_t ring;    // block-table rows are rings of max_blocks pages
 };
 
 template <typename T>
@@ -180,7 +180,9 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
           x2[i] = x2[i] * inv * (double)r.w[H + lane * C + i];
         }
       }
-      if (r.kind != 2 && rope) {
+      // keys are stored unrotated in the exact K=V form (k_eq_v = 2): the attention kernels
+      // rotate them for the scores and read them unrotated as values
+      if (rope && (r.kind == 0 || (r.kind == 1 && a.k_eq_v != 2))) {
 #pragma unroll
         for (int i = 0; i < C; ++i) {
           const double cs = cos_t[lane * C + i], sn = sin_t[lane * C + i];

@@ -32,8 +32,13 @@ struct KvWriteLaunch {
 // Shared description of an attention call (decode or prefill).
 struct AttnLaunch {
   bool dtype_bf16;
-  int D, Hq, Hkv, window, k_eq_v;
+  int D, Hq, Hkv, window, k_eq_v;  // k_eq_v: 0 separate V, 1 K=V, 2 exact K=V
   float scale, softcap;
+  // exact K=V (k_eq_v = 2): rotation of the stored keys and the value factor w_v / w_k
+  float rope_theta, rope_scale;
+  int rope_angles;
+  const float* kv_kw;
+  const float* kv_vw;
   const void* q;
   const int32_t* cu_seqlens_q;  // prefill only
   const void* k_cache;

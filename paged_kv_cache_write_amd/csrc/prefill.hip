@@ -91,6 +91,13 @@ struct TileLds {
   static_assert(SK >= 2 && SK <= kMaxStages && (KEQV ? SK >= 3 : (SV >= 2 && SV <= SK)),
                 "ring depths");
   static_assert(kBytes <= kBudget, "LDS budget");
+  // exact K=V: the rotated rope units of the two tiles of an iteration, laid out like a K tile
+  // of 16 unit columns (the 8 holding dimensions 0-63, then their 8 partners D/2 further)
+  static constexpr int kRopePage = 16 * 256;
+  static constexpr int kRopeTile = 2 * kRopePage;
+  static constexpr int kRopeOff = kBytes;
+  static constexpr int kRopeLo = 2 * kRopeTile;  // the lo terms, after the hi terms
+  static constexpr int kRopeBytes = 4 * kRopeTile;
 };
 
 // Copy i (0 .. kPerWave-1) of this wave for one tile of K (V=false) or of V^T (V=true) into
@@ -138,7 +145,20 @@ __device__ __forceinline__ void zero_tail_values(unsigned char* tile, int nvalid
   }
 }
 
-template <int D, int SM, bool KEQV>
+// Exact K=V: the chunk of QK^T fragment f in the rope buffer (chunks 0 and 1, holding
+// dimensions 0-63, and their partners NC/2 and NC/2 + 1 become 0 .. 3), -1 for the fragments
+// read from the K tile.
+template <int NC, int f>
+constexpr int rope_chunk_of() {
+  constexpr int c = f >> 1;
+  return c < 2 ? c : (c >= NC / 2 && c < NC / 2 + 2 ? c - NC / 2 + 2 : -1);
+}
+
+// EXACT (with KEQV): keys are stored unrotated.  After each iteration's tiles have landed, the
+// workgroup rotates their units holding dimensions 0-63 and the partners of those (one unit
+// pair per thread) into a separate LDS buffer that the QK^T fragment reads of those chunks
+// use; the values are still read from the unrotated tile.
+template <int D, int SM, bool KEQV, bool EXACT>
 __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs a, int tiles_per_bg,
                                                                      int n_tiles) {
   using T = TileLds<D, KEQV>;
@@ -221,6 +241,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
 
   const int64_t bt_row = (int64_t)b * a.max_blocks;
   const int last_page = (L - 1) / kPage;
+  // exact K=V: this thread's unit pair in the rotation pass (row, unit column, page, tile of
+  // the iteration)
+  const int rp_r = threadIdx.x & 15, rp_x = (threadIdx.x >> 4) & 7;
+  const int rp_p = (threadIdx.x >> 7) & 1, rp_u = threadIdx.x >> 8;
 
   // Lane offsets inside a tile (bytes); fragment c / column block nn adds an immediate.
   //   K, product m: row qk_row_key(c16, m) of page c16 / 8, chunk 4c + j.
@@ -231,6 +255,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
   for (int m = 0; m < 2; ++m)
     koff[m] = kpage * T::kPageBytes + 256 * j + 16 * ((qk_row_key(c16, m) + 4 * kpage) & 15);
   const int voff = (j >> 1) * T::kPageBytes + c16 * 32 + (j & 1) * 16;
+  // exact K=V: the same lane offsets in the rope buffer (pages of 16 units): koff[m] - rdiff
+  const int rdiff = kpage * (T::kPageBytes - T::kRopePage);
   // key of score slot e (product e / 4, register e % 4) of this lane group, minus k0
   const int kslot = (j >> 1) * kPage + 8 * (j & 1);
 
@@ -299,6 +325,17 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
     const int k0 = (kt0 + t) * kTileKeys;
     const unsigned char* kt = smem + T::kKRing + (t % S) * T::kTile;
     const unsigned char* vt = smem + T::kVRing + (t % S) * T::kTile + voff;
+    const unsigned char* rt = smem + T::kRopeOff + (t % 2) * T::kRopeTile;
+    // K fragment f (chunk c = f / 2, product m = f % 2); exact K=V reads the chunks holding
+    // dimensions 0-63 and their partners from the rotated copies
+    auto kread = [&](auto fc) -> bf16x8_t {
+      constexpr int f = decltype(fc)::value, c = f >> 1;
+      constexpr int rc = EXACT ? rope_chunk_of<NC, f>() : -1;
+      if constexpr (rc >= 0)
+        return as_bf16x8(*(const u32x4_t*)(rt - rdiff + koff[f & 1] + 1024 * rc));
+      else
+        return as_bf16x8(*(const u32x4_t*)(kt + koff[f & 1] + 1024 * c));
+    };
 
     // ---- S^T = K Q^T: s[m][rb], product m covering the key rows described above.  One
     // chunk per K fragment f (c = f / 2, m = f % 2): its R products, the read of fragment
@@ -308,21 +345,32 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
     bf16x8_t kf[2 * NC];
     sfor<kPF>([&](auto fc) {
       constexpr int f = decltype(fc)::value;
-      kf[f] = as_bf16x8(*(const u32x4_t*)(kt + koff[f & 1] + 1024 * (f >> 1)));
+      kf[f] = kread(fc);
     });
     sfor<2 * NC>([&](auto fc) {
       constexpr int f = decltype(fc)::value;
-      if constexpr (f + kPF < 2 * NC)
-        kf[f + kPF] =
-            as_bf16x8(*(const u32x4_t*)(kt + koff[(f + kPF) & 1] + 1024 * ((f + kPF) >> 1)));
+      if constexpr (f + kPF < 2 * NC) kf[f + kPF] = kread(std::integral_constant<int, f + kPF>{});
       sfor<(f + 1) * Q / (2 * NC) - f * Q / (2 * NC)>([&](auto qc) {
         constexpr int q = f * Q / (2 * NC) + decltype(qc)::value;
         k_chunk(ct + q / T::kPerWave, cids[q / T::kPerWave], q % T::kPerWave);
       });
+      constexpr int rc = EXACT ? rope_chunk_of<NC, f>() : -1;
+      if constexpr (rc >= 0) {  // the lo terms of a rotated fragment
+        const bf16x8_t lo =
+            as_bf16x8(*(const u32x4_t*)(rt + T::kRopeLo - rdiff + koff[f & 1] + 1024 * rc));
 #pragma unroll
-      for (int rb = 0; rb < R; ++rb)
-        s[f & 1][rb] = mfma_16x16x32(kf[f], qf[rb][f >> 1],
-                                     f < 2 ? float4_t{0.f, 0.f, 0.f, 0.f} : s[f & 1][rb]);
+        for (int rb = 0; rb < R; ++rb)
+          s[f & 1][rb] = mfma_16x16x32(lo, qf[rb][f >> 1],
+                                       f < 2 ? float4_t{0.f, 0.f, 0.f, 0.f} : s[f & 1][rb]);
+#pragma unroll
+        for (int rb = 0; rb < R; ++rb)
+          s[f & 1][rb] = mfma_16x16x32(kf[f], qf[rb][f >> 1], s[f & 1][rb]);
+      } else {
+#pragma unroll
+        for (int rb = 0; rb < R; ++rb)
+          s[f & 1][rb] = mfma_16x16x32(kf[f], qf[rb][f >> 1],
+                                       f < 2 ? float4_t{0.f, 0.f, 0.f, 0.f} : s[f & 1][rb]);
+      }
       fence_sched();
     });
     // the first V^T fragments of this tile's P.V, read while the softmax runs
@@ -404,21 +452,19 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
         fence_sched();
       });
     } else {
-      // values are the keys: gather K[key][d] column-wise from the chunk-major K page;
-      // key 8 (j % 2) + e of page j / 2 at d = 16 nn + c16
-      const int pg = j >> 1;
-      const int kb = pg * T::kPageBytes + 256 * (c16 >> 3) + 2 * (c16 & 7);
-      const int rot = 8 * (j & 1) + 4 * pg;
+      // values are the keys: the V^T fragment (d = 16 nn + c16, keys 8 (j % 2) .. + 7 of page
+      // j / 2) comes from the chunk-major K page by two transposing reads.  Lane 4e + q of a
+      // group points at dimensions 16 nn + 4q .. + 3 (half q % 2 of unit 2 nn + q / 2) of key
+      // 8 (j % 2) + e (first read) or + 4 + e (second read).
+      const int pg = j >> 1, e4 = c16 >> 2, q4 = c16 & 3;
+      const int vb = pg * T::kPageBytes + 256 * (q4 >> 1) + 8 * (q4 & 1);
+      const int vr0 = vb + 16 * ((8 * (j & 1) + e4 + 4 * pg) & 15);
+      const int vr1 = vb + 16 * ((8 * (j & 1) + 4 + e4 + 4 * pg) & 15);
 #pragma unroll
       for (int nn = 0; nn < ND; ++nn) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const unsigned char* p0 = kt + kb + 512 * nn + 16 * ((rot + 2 * e2) & 15);
-          const unsigned char* p1 = kt + kb + 512 * nn + 16 * ((rot + 2 * e2 + 1) & 15);
-          w[e2] = (uint32_t)(*(const uint16_t*)p0) | ((uint32_t)(*(const uint16_t*)p1) << 16);
-        }
-        const bf16x8_t af = as_bf16x8(u32x4_t{w[0], w[1], w[2], w[3]});
+        const u32x2_t lo = lds_read_tr16(kt + vr0 + 512 * nn);
+        const u32x2_t hi = lds_read_tr16(kt + vr1 + 512 * nn);
+        const bf16x8_t af = as_bf16x8(u32x4_t{lo.x, lo.y, hi.x, hi.y});
 #pragma unroll
         for (int rb = 0; rb < R; ++rb) o[rb][nn] = mfma_16x16x32(af, pf[rb], o[rb][nn]);
       }
@@ -446,6 +492,29 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
         __syncthreads();
       }
     }
+    if constexpr (EXACT) {
+      // the rotated rope units of this iteration's tiles (the previous iteration's readers of
+      // the buffer have all passed the barrier above)
+      static_assert(TB == 2, "one rope buffer per tile of an iteration");
+      const int tl = TB * jj + rp_u;
+      if (tl < np) {
+        const int rot = 16 * ((rp_r + 4 * rp_p) & 15);
+        const unsigned char* src =
+            smem + T::kKRing + (tl % S) * T::kTile + rp_p * T::kPageBytes + rot;
+        u32x4_t ua = *(const u32x4_t*)(src + 256 * rp_x);
+        u32x4_t ub = *(const u32x4_t*)(src + 256 * (rp_x + D / 16));
+        u32x4_t la = {0u, 0u, 0u, 0u}, lb = {0u, 0u, 0u, 0u};
+        const int64_t pos = (int64_t)(kt0 + tl) * kTileKeys + rp_p * kPage + rp_r;
+        rope_units_exact(ua, ub, la, lb, rp_x, rope_rho(a.rho0, a.rho_step, 8 * rp_x),
+                         a.rho_step, a.rope_pairs, pos);
+        unsigned char* dst = smem + T::kRopeOff + rp_u * T::kRopeTile + rp_p * T::kRopePage + rot;
+        *(u32x4_t*)(dst + 256 * rp_x) = ua;
+        *(u32x4_t*)(dst + 256 * (8 + rp_x)) = ub;
+        *(u32x4_t*)(dst + T::kRopeLo + 256 * rp_x) = la;
+        *(u32x4_t*)(dst + T::kRopeLo + 256 * (8 + rp_x)) = lb;
+      }
+      __syncthreads();
+    }
     // Every wave runs every tile of the workgroup's range: a tile outside a wave's band is
     // masked whole (its weights are exactly 0) and costs a little matrix-core time, where a
     // branch around the work would split the copy schedule spread over it.
@@ -472,42 +541,57 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
     const float inv = 1.0f / l;
     uint16_t* dst = a.out + ((int64_t)(q0 + i) * a.Hq + g * G + hh) * D + 4 * j;
 #pragma unroll
-    for (int nn = 0; nn < ND; ++nn)
+    for (int nn = 0; nn < ND; ++nn) {
+      float f[4] = {inv, inv, inv, inv};
+      if constexpr (EXACT) {
+        if (a.kv_vw) {  // values are the stored keys times w_v / w_k
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            f[e] *= a.kv_vw[16 * nn + 4 * j + e] / a.kv_kw[16 * nn + 4 * j + e];
+        }
+      }
       *(u32x2_t*)(dst + 16 * nn) =
-          u32x2_t{pack_bf16x2(o[rb][nn][0] * inv, o[rb][nn][1] * inv),
-                  pack_bf16x2(o[rb][nn][2] * inv, o[rb][nn][3] * inv)};
+          u32x2_t{pack_bf16x2(o[rb][nn][0] * f[0], o[rb][nn][1] * f[1]),
+                  pack_bf16x2(o[rb][nn][2] * f[2], o[rb][nn][3] * f[3])};
+    }
   }
 }
 
-template <int D, int SM, bool KEQV>
+template <int D, int SM, bool KEQV, bool EXACT>
 hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   using T = TileLds<D, KEQV>;
+  constexpr int kLds = T::kBytes + (EXACT ? T::kRopeBytes : 0);
   constexpr int kRowsPerWg = Rows<D>::kPerWg;
   const int tiles_per_bg = (a.max_q_len * a.G + kRowsPerWg - 1) / kRowsPerWg;
   const int n_tiles = tiles_per_bg * a.Hkv * a.batch;
   if (n_tiles == 0) return hipSuccess;
   const int grid = (n_tiles + 7) / 8 * 8;  // whole rounds over the 8 XCDs
-  static_assert(T::kBytes <= 160 * 1024, "LDS budget");
+  static_assert(kLds <= 160 * 1024, "LDS budget");
   hipError_t e = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&prefill_tiled_kernel<D, SM, KEQV>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, T::kBytes);
+      reinterpret_cast<const void*>(&prefill_tiled_kernel<D, SM, KEQV, EXACT>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((prefill_tiled_kernel<D, SM, KEQV>), dim3(grid), dim3(64 * kWaves),
-                     T::kBytes, s, a, tiles_per_bg, n_tiles);
+  hipLaunchKernelGGL((prefill_tiled_kernel<D, SM, KEQV, EXACT>), dim3(grid), dim3(64 * kWaves),
+                     kLds, s, a, tiles_per_bg, n_tiles);
   return hipGetLastError();
 }
 
 template <int D, int SM>
-hipError_t by_keqv(const AttnArgs& a, bool keqv, hipStream_t s) {
-  return keqv ? launch_t<D, SM, true>(a, s) : launch_t<D, SM, false>(a, s);
+hipError_t by_kv(const AttnArgs& a, int kv_mode, hipStream_t s) {
+  switch (kv_mode) {
+    case 0: return launch_t<D, SM, false, false>(a, s);
+    case 1: return launch_t<D, SM, true, false>(a, s);
+    case 2: return launch_t<D, SM, true, true>(a, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int D>
-hipError_t by_flags(const AttnArgs& a, bool cap, bool keqv, hipStream_t s) {
-  if (cap) return by_keqv<D, kScoreCap>(a, keqv, s);
+hipError_t by_flags(const AttnArgs& a, bool cap, int kv_mode, hipStream_t s) {
+  if (cap) return by_kv<D, kScoreCap>(a, kv_mode, s);
   // a positive scale commutes with the max, so it can be applied inside the exponent
-  return a.sc.c_scale > 0.f ? by_keqv<D, kScoreFold>(a, keqv, s)
-                            : by_keqv<D, kScorePlain>(a, keqv, s);
+  return a.sc.c_scale > 0.f ? by_kv<D, kScoreFold>(a, kv_mode, s)
+                            : by_kv<D, kScorePlain>(a, kv_mode, s);
 }
 
 }  // namespace
@@ -516,11 +600,11 @@ hipError_t launch_prefill(const AttnLaunch& L, hipStream_t s) {
   if (L.batch == 0 || L.total_q == 0) return hipSuccess;
   if (!L.dtype_bf16) return launch_attn_f32(L, false, s);
   const AttnArgs a = make_attn_args(L);
-  const bool cap = L.softcap > 0.f, keqv = L.k_eq_v != 0;
+  const bool cap = L.softcap > 0.f;
   switch (L.D) {
-    case 128: return by_flags<128>(a, cap, keqv, s);
-    case 256: return by_flags<256>(a, cap, keqv, s);
-    case 512: return by_flags<512>(a, cap, keqv, s);
+    case 128: return by_flags<128>(a, cap, L.k_eq_v, s);
+    case 256: return by_flags<256>(a, cap, L.k_eq_v, s);
+    case 512: return by_flags<512>(a, cap, L.k_eq_v, s);
   }
   return hipErrorInvalidValue;
 }

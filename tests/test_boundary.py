@@ -157,6 +157,24 @@ def test_ring_tables_are_sized_on_the_host():
     assert call_decode(good(window=1024), max_blocks=65, max_context_len=36000)[0] == INVALID
 
 
+def test_exact_kv_params_are_checked():
+    """k_eq_v = 2 (exact K=V): both value-factor weights or neither, at most 64 rotated pairs;
+    the weights belong to that mode only."""
+    assert call_decode(good(k_eq_v=3), v_cache=None)[0] == INVALID
+    p = good(k_eq_v=1)
+    p.kv_k_norm_w = 0x1000
+    assert call_decode(p, v_cache=None)[0] == INVALID
+    p = good(k_eq_v=2, head_dim=512, num_kv_heads=2, rope_theta=1e6, rope_angles=64)
+    p.kv_k_norm_w = 0x1000
+    st, err = call_decode(p, v_cache=None)
+    assert st == INVALID and "both" in err
+    p = good(k_eq_v=2, head_dim=512, num_kv_heads=2, rope_theta=1e6)  # all 256 pairs rotate
+    st, err = call_decode(p, v_cache=None)
+    assert st == UNSUPPORTED and "64" in err
+    assert call_decode(good(k_eq_v=2, rope_theta=0.0), v_cache=FAKE)[0] == INVALID
+    assert call_write(good(k_eq_v=2, rope_angles=64), v=FAKE)[0] == INVALID
+
+
 def test_prefill_rejects_bad_arguments():
     p = good()
     assert call_prefill(p, cu=None)[0] == INVALID
