@@ -1,9 +1,11 @@
 // kv_write.hip -- fused RMSNorm + rotary embedding + paged scatter.
 //
 // A workgroup owns one token and a group of its head slots (q heads, then k heads, then v
-// heads).  It first computes the token's rotation table -- cos and sin of t * omega_k for the
-// D/2 frequencies, in double precision -- once into LDS, then each of its 4 wavefronts takes
-// one (token, head) row at a time.  Large batches give a workgroup all slots of its token;
+// heads).  Each wave issues the loads of its first rows before anything else (they depend only
+// on the token); then one parallel probe finds the owning sequence and its length, the
+// workgroup computes the token's rotation table -- cos and sin of t * omega_k for the D/2
+// frequencies, in double precision -- once into LDS, and each of its 4 wavefronts takes one
+// (token, head) row at a time.  Large batches give a workgroup all slots of its token;
 // small ones (a decode step) split a token's slots over several workgroups so that the launch
 // still fills the chip.  Each wave issues the loads of 4 rows before it processes the first.  With rotate-half RoPE the
 // pair (k, k + D/2) must sit in one lane, so lane l holds the C = D/128 consecutive elements
@@ -104,18 +106,41 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
   const int group = (int)(blockIdx.x - tok * a.groups);
   if (tok >= a.total_tokens) return;
 
+  // this wave's first kRowsInFlight rows are loaded before anything else: they depend only on
+  // the token, so their latency overlaps the sequence lookup and the rotation table
+  const int s0 = group * a.slots_per_wg;
+  const int s1 = s0 + a.slots_per_wg < a.nslots ? s0 + a.slots_per_wg : a.nslots;
+  constexpr int U = kRowsInFlight;
+  Row<T, C> rows[U];
+  auto load_rows = [&](int first) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int slot = first + 4 * u;
+      rows[u].valid = slot < s1;
+      if (rows[u].valid) rows[u].locate(a, slot, tok, D);
+      if (rows[u].valid) rows[u].template load<H>(lane);
+    }
+  };
+  load_rows(s0 + wave);
+
   // sequence that owns this token: the b with cu[b] <= tok < cu[b + 1] (one parallel probe
-  // per sequence instead of a chain of dependent loads; empty sequences never match)
+  // per sequence instead of a chain of dependent loads; empty sequences never match).  The
+  // probe also fetches the owner's context length, so the position is known after one round.
   __shared__ int owner;
+  __shared__ int64_t own_t;
   if (threadIdx.x == 0) owner = -1;
   __syncthreads();
-  for (int i = threadIdx.x; i < a.batch; i += 256)
-    if (a.cu[i] <= tok && tok < a.cu[i + 1]) owner = i;
+  for (int i = threadIdx.x; i < a.batch; i += 256) {
+    const int c0 = a.cu[i], c1 = a.cu[i + 1], len = a.ctx[i];
+    if (c0 <= tok && tok < c1) {
+      owner = i;
+      own_t = (int64_t)len - (c1 - c0) + (tok - c0);
+    }
+  }
   __syncthreads();
   const int b = owner;
   if (b < 0) return;  // tok beyond cu[batch]: nothing owns it
-  const int64_t n = (int64_t)a.cu[b + 1] - a.cu[b];
-  const int64_t t = (int64_t)a.ctx[b] - n + (tok - a.cu[b]);
+  const int64_t t = own_t;
   const int64_t page = t >> 4;
   if (t < 0) return;  // inconsistent metadata: write nothing
   int64_t blk = 0;
@@ -144,20 +169,10 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
   }
   __syncthreads();
 
-  const int s0 = group * a.slots_per_wg;
-  const int s1 = s0 + a.slots_per_wg < a.nslots ? s0 + a.slots_per_wg : a.nslots;
   // the rows of this wave, kRowsInFlight at a time: all their loads are issued before the
   // first row is processed
-  constexpr int U = kRowsInFlight;
   for (int first = s0 + wave; first < s1; first += 4 * U) {
-    Row<T, C> rows[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int slot = first + 4 * u;
-      rows[u].valid = slot < s1;
-      if (rows[u].valid) rows[u].locate(a, slot, tok, D);
-      if (rows[u].valid) rows[u].template load<H>(lane);
-    }
+    if (first != s0 + wave) load_rows(first);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (!rows[u].valid) continue;
@@ -253,6 +268,7 @@ hipError_t launch_kv_write(const KvWriteLaunch& L, hipStream_t s) {
   a.nslots = (a.has_q ? L.Hq : 0) + (a.has_kv ? L.Hkv + (L.k_eq_v ? 0 : L.Hkv) : 0);
   a.theta = (double)L.rope_theta;
   a.rope_angles = L.rope_angles;
+
   a.pos_scale = (double)L.rope_scale;
   a.eps = (double)L.rms_eps;
   const bool bf = L.dtype_bf16;
