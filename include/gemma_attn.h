@@ -52,11 +52,12 @@
  *   attention calls refuse smaller rings; ga_kv_cache_write cannot know the chunk a later call
  *   attends with, so sizing the ring is the caller's part there.
  *   A key page is kept in 16-byte units: unit (row r, x) holds elements x*U .. x*U+U-1 of key
- *   row r (U = 8 for bf16, 4 for fp32) at unit slot 16*x + (r + 4*(lp % 2)) % 16 of the page,
- *   i.e. the 16 rows of one unit column are contiguous (256 bytes) and pages of odd logical
- *   index have their rows rotated by 4.  This is the order in which a 32-key tile (an even
- *   page, then an odd one) is read by the matrix cores without LDS bank conflicts, so a tile is
- *   copied to LDS as whole contiguous 1 KiB runs.
+ *   row r (U = 8 for bf16, 4 for fp32) at unit slot 16*x + (r + 4*(lp % 2) + 4*((x/8) % 2)) % 16
+ *   of the page, i.e. the 16 rows of one unit column are contiguous (256 bytes) and the rows are
+ *   rotated by 4 on pages of odd logical index and again in unit columns whose bit 3 is set.
+ *   This is the order in which a 32-key tile (an even page, then an odd one) is read without
+ *   LDS bank conflicts by the matrix-core score operands and, in the K=V forms, by the
+ *   transposing value reads, so a tile is copied to LDS as whole contiguous 1 KiB runs.
  *   The value page is stored transposed so that the matrix-core operand of P.V reads 16
  *   contiguous bytes per lane; with k_eq_v there is no v_cache and values are read from k_cache.
  */

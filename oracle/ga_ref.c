@@ -42,8 +42,9 @@
  * Memory layout of the paged cache (the library's documented format):
  *   K page: k_cache[blk][g][16 rows x D], stored in 16-byte units: unit (row off, x) holds
  *           elements d = x*U .. x*U+U-1 of key row off (U = 8 for bf16, 4 for fp32) and
- *           sits at unit slot 16*x + ((off + 4*(lp % 2)) % 16) of the page, lp = pos / 16 being
- *           the page's logical index in its sequence (rows of odd pages rotated by 4).
+ *           sits at unit slot 16*x + ((off + 4*(lp % 2) + 4*((x / 8) % 2)) % 16) of the page,
+ *           lp = pos / 16 being the page's logical index in its sequence (rows rotated by 4
+ *           on odd pages and again in unit columns whose bit 3 is set).
  *   V page: v_cache[blk][g][d][off]   -- d-major, the 16 (block_size) keys of a page contiguous.
  *   With k_eq_v the V operand is read from k_cache.
  * dtype code: 0 = fp32 (float storage), 1 = bf16 (uint16_t storage, round-to-nearest-even).
@@ -143,8 +144,9 @@ static int64_t k_index(int64_t blk, int64_t off, int g, int d, int Hkv, int bs, 
                        int64_t pos) {
   const int64_t U = dtype == 1 ? 8 : 4; /* elements per 16-byte unit */
   const int64_t lp = pos / bs;
-  const int64_t row_slot = (off + 4 * (lp % 2)) % bs;
-  const int64_t unit = (d / U) * bs + row_slot;
+  const int64_t x = d / U; /* unit column */
+  const int64_t row_slot = (off + 4 * (lp % 2) + 4 * ((x / 8) % 2)) % bs;
+  const int64_t unit = x * bs + row_slot;
   return (blk * Hkv + g) * bs * (int64_t)D + unit * U + d % U;
 }
 

@@ -89,9 +89,11 @@ __device__ __forceinline__ void decode_piece(const AttnArgs& a, const bf16x8_t (
   };
 
   // page bases are wave-uniform (scalar registers); each lane adds one 32-bit offset
-  // K unit (row c16, column 4c + j) of a page of logical parity par: k_page_elem layout
+  // K unit (row c16, column 4c + j) of a page of logical parity par: k_page_elem layout, row
+  // slot c16 + 4 par + 4 ((c / 2) mod 2), i.e. one of three lane offsets
   const uint32_t koff0 = (uint32_t)(128 * j + 8 * c16);
   const uint32_t koff1 = (uint32_t)(128 * j + 8 * ((c16 + 4) & 15));
+  const uint32_t koff2 = (uint32_t)(128 * j + 8 * ((c16 + 8) & 15));
   const uint32_t voff = (uint32_t)(c16 * kPage + 4 * j);
   const int64_t kpage = (int64_t)kPage * D;  // elements per (page, kv head)
   R r;
@@ -100,9 +102,10 @@ __device__ __forceinline__ void decode_piece(const AttnArgs& a, const bf16x8_t (
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const uint16_t* kp = a.kc + (blk_of(s, p) * a.Hkv + head_off) * kpage;
-      const uint32_t koff = ((pbeg + s * NP + p) & 1) ? koff1 : koff0;
+      const bool odd = ((pbeg + s * NP + p) & 1) != 0;
+      const uint32_t kA = odd ? koff1 : koff0, kB = odd ? koff2 : koff1;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) r.k[p][c] = ld16(kp + koff + 512 * c);
+      for (int c = 0; c < NC; ++c) r.k[p][c] = ld16(kp + (((c >> 1) & 1) ? kB : kA) + 512 * c);
     }
   };
   auto issue_v = [&](int s) {

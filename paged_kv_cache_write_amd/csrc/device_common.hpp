@@ -76,16 +76,21 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
 // ------------------------------------------------------------------------ K page layout -----
 // A K page (16 keys of one kv head) is stored in 16-byte units: unit (row r, x) holds elements
 // [x U, x U + U) of key row r, U = 16 / element size (8 for bf16, 4 for fp32), and sits at
-// byte 256 x + 16 ((r + 4 (lp mod 2)) mod 16) of the page, lp being the page's logical index
-// (position / 16) in its sequence.  So the 16 rows of one unit column x form one 256-byte
-// run, a 1 KiB run holds four consecutive unit columns of all 16 rows, and pages of odd
-// logical index have their rows rotated by 4: a 32-key tile (an even page, then an odd one)
-// copied to LDS as it is stored lets the 16 lanes of a matrix-core fragment read (8 rows of
-// each page, one unit column) hit 16 distinct bank groups.
+// byte 256 x + 16 k_slot(r, x, lp) of the page, lp being the page's logical index
+// (position / 16) in its sequence: the 16 rows of one unit column x form one 256-byte run and
+// a 1 KiB run holds four consecutive unit columns of all 16 rows.  The rows are rotated by 4
+// on pages of odd logical index and again in unit columns whose bit 3 is set.  A 32-key tile
+// (an even page, then an odd one) copied to LDS as it is stored is then read without bank
+// conflicts both by the score fragments (16 lanes: 8 rows of each page, one unit column) and,
+// in the K=V forms, by the transposing value reads (16 lanes: 4 rows of units x and x + 8).
+__device__ __forceinline__ int k_slot(int r, int x, int64_t lp) {
+  return (r + 4 * (int)(lp & 1) + 4 * ((x >> 3) & 1)) & 15;
+}
 template <int ESIZE>
 __device__ __forceinline__ int64_t k_page_elem(int r, int d, int64_t lp) {
   constexpr int U = 16 / ESIZE;
-  return (int64_t)(d / U) * (16 * U) + (int64_t)((r + 4 * (int)(lp & 1)) & 15) * U + (d % U);
+  const int x = d / U;
+  return (int64_t)x * (16 * U) + (int64_t)k_slot(r, x, lp) * U + (d % U);
 }
 
 // Block-table column of logical page lp: lp itself, or lp mod max_blocks when the table row is

@@ -18,7 +18,8 @@
 // owns its cache norms k, rotates q and k, norms v), §6.3 (slot = page id * 16 + row), §6.4
 // (per-token scatter into the cache).  [MNN] = "MNN 支持 Gemma4 全系列", §6.1 (q, k and v norms).
 // Layout of the pages: K [blk][g] in 16-byte units, chunk-major, rows rotated by 4 on odd
-// logical pages (k_page_elem); V [blk][g][d][row] (transposed page).
+// logical pages and in unit columns with bit 3 set (k_page_elem); V [blk][g][d][row]
+// (transposed page).
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -145,9 +146,9 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
   if (t < 0) return;  // inconsistent metadata: write nothing
   int64_t blk = 0;
   if (a.has_kv) {
-    if (!a.ring && page >= a.max_blocks) return;
+    if (!a.ring && page >= a.max_blocks) return;  // (all the exits are workgroup-uniform)
+    // the block id is checked after the rotation table, which its load latency overlaps
     blk = a.bt[(int64_t)b * a.max_blocks + bt_col((int)page, a.max_blocks, a.ring)];
-    if (blk < 0 || blk >= a.num_blocks) return;  // (all the exits are workgroup-uniform)
   }
   const int64_t off = t & 15;
 
@@ -167,6 +168,7 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
       sin_t[k] = sn;
     }
   }
+  if (a.has_kv && (blk < 0 || blk >= a.num_blocks)) return;  // no slot to write: nothing
   __syncthreads();
 
   // the rows of this wave, kRowsInFlight at a time: all their loads are issued before the

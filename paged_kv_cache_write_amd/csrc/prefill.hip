@@ -134,15 +134,23 @@ __device__ __forceinline__ void zero_tail_values(unsigned char* tile, int nvalid
           *(uint16_t*)(row + 2 * r) = 0;
     }
   } else {
-    // chunk-major K page: 16-byte unit (row r, chunk x) at 256 x + 16 ((r + 4 page) mod 16)
+    // chunk-major K page: 16-byte unit (row r, chunk x) at 256 x + 16 k_slot(r, x, page)
     for (int q = threadIdx.x; q < 2 * kPage * (D / 8); q += 64 * kWaves) {
       const int page = q / (kPage * (D / 8)), u = q - page * (kPage * (D / 8));
       const int x = u >> 4, r = u & 15;
       if (page * kPage + r >= nvalid)
-        *(u32x4_t*)(tile + page * T::kPageBytes + 256 * x + 16 * ((r + 4 * page) & 15)) =
+        *(u32x4_t*)(tile + page * T::kPageBytes + 256 * x + 16 * k_slot(r, x, page)) =
             u32x4_t{0u, 0u, 0u, 0u};
     }
   }
+}
+
+// K=V value fragment nn: the 16 dimensions of K units x0 = kv_block_unit(nn) and x0 + 8 (units
+// whose bit 3 is clear, paired with the unit 8 above: every unit belongs to one fragment).  A
+// row i (and output row i of O^T) of the fragment is dimension kv_block_dim(nn, i).
+__device__ __forceinline__ constexpr int kv_block_unit(int nn) { return (nn & 7) + 16 * (nn >> 3); }
+__device__ __forceinline__ constexpr int kv_block_dim(int nn, int i) {
+  return 8 * (kv_block_unit(nn) + 8 * (i >> 3)) + (i & 7);
 }
 
 // Exact K=V: the chunk of QK^T fragment f in the rope buffer (chunks 0 and 1, holding
@@ -250,10 +258,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
   //   K, product m: row qk_row_key(c16, m) of page c16 / 8, chunk 4c + j.
   //   V^T: row d = 16 nn + c16 of page j / 2, the 8 keys 8 (j % 2) .. + 7.
   const int kpage = c16 >> 3;
-  int koff[2];
+  // (koff[m][cb]: unit columns 4c + j with bit 3 = cb, i.e. cb = (c / 2) mod 2)
+  int koff[2][2];
 #pragma unroll
   for (int m = 0; m < 2; ++m)
-    koff[m] = kpage * T::kPageBytes + 256 * j + 16 * ((qk_row_key(c16, m) + 4 * kpage) & 15);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+      koff[m][cb] = kpage * T::kPageBytes + 256 * j +
+                    16 * ((qk_row_key(c16, m) + 4 * kpage + 4 * cb) & 15);
   const int voff = (j >> 1) * T::kPageBytes + c16 * 32 + (j & 1) * 16;
   // exact K=V: the same lane offsets in the rope buffer (pages of 16 units): koff[m] - rdiff
   const int rdiff = kpage * (T::kPageBytes - T::kRopePage);
@@ -332,9 +344,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
       constexpr int f = decltype(fc)::value, c = f >> 1;
       constexpr int rc = EXACT ? rope_chunk_of<NC, f>() : -1;
       if constexpr (rc >= 0)
-        return as_bf16x8(*(const u32x4_t*)(rt - rdiff + koff[f & 1] + 1024 * rc));
+        return as_bf16x8(
+            *(const u32x4_t*)(rt - rdiff + koff[f & 1][(rc >> 1) & 1] + 1024 * rc));
       else
-        return as_bf16x8(*(const u32x4_t*)(kt + koff[f & 1] + 1024 * c));
+        return as_bf16x8(*(const u32x4_t*)(kt + koff[f & 1][(c >> 1) & 1] + 1024 * c));
     };
 
     // ---- S^T = K Q^T: s[m][rb], product m covering the key rows described above.  One
@@ -356,8 +369,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
       });
       constexpr int rc = EXACT ? rope_chunk_of<NC, f>() : -1;
       if constexpr (rc >= 0) {  // the lo terms of a rotated fragment
-        const bf16x8_t lo =
-            as_bf16x8(*(const u32x4_t*)(rt + T::kRopeLo - rdiff + koff[f & 1] + 1024 * rc));
+        const bf16x8_t lo = as_bf16x8(*(const u32x4_t*)(rt + T::kRopeLo - rdiff +
+                                                         koff[f & 1][(rc >> 1) & 1] + 1024 * rc));
 #pragma unroll
         for (int rb = 0; rb < R; ++rb)
           s[f & 1][rb] = mfma_16x16x32(lo, qf[rb][f >> 1],
@@ -452,18 +465,19 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
         fence_sched();
       });
     } else {
-      // values are the keys: the V^T fragment (d = 16 nn + c16, keys 8 (j % 2) .. + 7 of page
-      // j / 2) comes from the chunk-major K page by two transposing reads.  Lane 4e + q of a
-      // group points at dimensions 16 nn + 4q .. + 3 (half q % 2 of unit 2 nn + q / 2) of key
-      // 8 (j % 2) + e (first read) or + 4 + e (second read).
+      // values are the keys: V^T fragment nn covers the 16 dimensions of units x0(nn) and
+      // x0(nn) + 8 (kv_block_unit; A row i is dimension kv_block_dim(nn, i)), keys 8 (j % 2) ..
+      // + 7 of page j / 2, by two transposing reads.  Lane 4e + q of a group points at half
+      // q % 2 of unit x0 + 8 (q / 2) of key 8 (j % 2) + e (first read) or + 4 + e (second);
+      // units x0 and x0 + 8 sit 4 row slots apart, so the reads are free of bank conflicts.
       const int pg = j >> 1, e4 = c16 >> 2, q4 = c16 & 3;
-      const int vb = pg * T::kPageBytes + 256 * (q4 >> 1) + 8 * (q4 & 1);
-      const int vr0 = vb + 16 * ((8 * (j & 1) + e4 + 4 * pg) & 15);
-      const int vr1 = vb + 16 * ((8 * (j & 1) + 4 + e4 + 4 * pg) & 15);
+      const int vb = pg * T::kPageBytes + 256 * 8 * (q4 >> 1) + 8 * (q4 & 1);
+      const int vr0 = vb + 16 * ((8 * (j & 1) + e4 + 4 * pg + 4 * (q4 >> 1)) & 15);
+      const int vr1 = vb + 16 * ((8 * (j & 1) + 4 + e4 + 4 * pg + 4 * (q4 >> 1)) & 15);
 #pragma unroll
       for (int nn = 0; nn < ND; ++nn) {
-        const u32x2_t lo = lds_read_tr16(kt + vr0 + 512 * nn);
-        const u32x2_t hi = lds_read_tr16(kt + vr1 + 512 * nn);
+        const u32x2_t lo = lds_read_tr16(kt + vr0 + 256 * kv_block_unit(nn));
+        const u32x2_t hi = lds_read_tr16(kt + vr1 + 256 * kv_block_unit(nn));
         const bf16x8_t af = as_bf16x8(u32x4_t{lo.x, lo.y, hi.x, hi.y});
 #pragma unroll
         for (int rb = 0; rb < R; ++rb) o[rb][nn] = mfma_16x16x32(af, pf[rb], o[rb][nn]);
@@ -498,20 +512,23 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
       static_assert(TB == 2, "one rope buffer per tile of an iteration");
       const int tl = TB * jj + rp_u;
       if (tl < np) {
-        const int rot = 16 * ((rp_r + 4 * rp_p) & 15);
-        const unsigned char* src =
-            smem + T::kKRing + (tl % S) * T::kTile + rp_p * T::kPageBytes + rot;
-        u32x4_t ua = *(const u32x4_t*)(src + 256 * rp_x);
-        u32x4_t ub = *(const u32x4_t*)(src + 256 * (rp_x + D / 16));
+        // source units rp_x and rp_x + D/16 of the K tile; in the rope buffer they become
+        // columns rp_x and 8 + rp_x (row slots by k_slot of those columns)
+        const unsigned char* src = smem + T::kKRing + (tl % S) * T::kTile + rp_p * T::kPageBytes;
+        u32x4_t ua = *(const u32x4_t*)(src + 256 * rp_x + 16 * k_slot(rp_r, rp_x, rp_p));
+        u32x4_t ub = *(const u32x4_t*)(src + 256 * (rp_x + D / 16) +
+                                       16 * k_slot(rp_r, rp_x + D / 16, rp_p));
         u32x4_t la = {0u, 0u, 0u, 0u}, lb = {0u, 0u, 0u, 0u};
         const int64_t pos = (int64_t)(kt0 + tl) * kTileKeys + rp_p * kPage + rp_r;
         rope_units_exact(ua, ub, la, lb, rp_x, rope_rho(a.rho0, a.rho_step, 8 * rp_x),
                          a.rho_step, a.rope_pairs, pos);
-        unsigned char* dst = smem + T::kRopeOff + rp_u * T::kRopeTile + rp_p * T::kRopePage + rot;
-        *(u32x4_t*)(dst + 256 * rp_x) = ua;
-        *(u32x4_t*)(dst + 256 * (8 + rp_x)) = ub;
-        *(u32x4_t*)(dst + T::kRopeLo + 256 * rp_x) = la;
-        *(u32x4_t*)(dst + T::kRopeLo + 256 * (8 + rp_x)) = lb;
+        unsigned char* dst = smem + T::kRopeOff + rp_u * T::kRopeTile + rp_p * T::kRopePage;
+        const int ra = 256 * rp_x + 16 * k_slot(rp_r, rp_x, rp_p);
+        const int rb = 256 * (8 + rp_x) + 16 * k_slot(rp_r, 8 + rp_x, rp_p);
+        *(u32x4_t*)(dst + ra) = ua;
+        *(u32x4_t*)(dst + rb) = ub;
+        *(u32x4_t*)(dst + T::kRopeLo + ra) = la;
+        *(u32x4_t*)(dst + T::kRopeLo + rb) = lb;
       }
       __syncthreads();
     }
@@ -539,18 +556,20 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
     const int row = wrow0 + 16 * rb + c16;
     const int i = row / G, hh = row - (row / G) * G;
     const float inv = 1.0f / l;
-    uint16_t* dst = a.out + ((int64_t)(q0 + i) * a.Hq + g * G + hh) * D + 4 * j;
+    uint16_t* dst = a.out + ((int64_t)(q0 + i) * a.Hq + g * G + hh) * D;
 #pragma unroll
     for (int nn = 0; nn < ND; ++nn) {
+      // output rows 4j .. 4j+3 of fragment nn: dimensions 16 nn + 4j (separate V^T pages) or
+      // kv_block_dim(nn, 4j) (values taken from the K tile) onwards
+      const int d0 = KEQV ? kv_block_dim(nn, 4 * j) : 16 * nn + 4 * j;
       float f[4] = {inv, inv, inv, inv};
       if constexpr (EXACT) {
         if (a.kv_vw) {  // values are the stored keys times w_v / w_k
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            f[e] *= a.kv_vw[16 * nn + 4 * j + e] / a.kv_kw[16 * nn + 4 * j + e];
+          for (int e = 0; e < 4; ++e) f[e] *= a.kv_vw[d0 + e] / a.kv_kw[d0 + e];
         }
       }
-      *(u32x2_t*)(dst + 16 * nn) =
+      *(u32x2_t*)(dst + d0) =
           u32x2_t{pack_bf16x2(o[rb][nn][0] * f[0], o[rb][nn][1] * f[1]),
                   pack_bf16x2(o[rb][nn][2] * f[2], o[rb][nn][3] * f[3])};
     }

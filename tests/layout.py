@@ -2,7 +2,8 @@
 
 A K page holds the 16 keys of one kv head in 16-byte units: unit (row r, x) holds elements
 x*U .. x*U+U-1 of key row r (U = 8 for bf16, 4 for fp32) and sits at unit slot
-16*x + (r + 4*(lp % 2)) % 16 of the page, lp being the page's logical index in its sequence.
+16*x + (r + 4*(lp % 2) + 4*((x // 8) % 2)) % 16 of the page, lp being the page's logical index in
+its sequence.
 V pages are [d][row] (the transposed page) and need no map.  Written for the tests only,
 independently of the library and of the oracle.
 """
@@ -19,7 +20,8 @@ def k_page_index(D: int, unit: int, parity: int) -> np.ndarray:
     """[16, D] element offsets inside a K page of logical parity `parity` for (row, d)."""
     r = np.arange(BS)[:, None]
     d = np.arange(D)[None, :]
-    return (d // unit) * (BS * unit) + ((r + 4 * parity) % BS) * unit + d % unit
+    x = d // unit
+    return x * (BS * unit) + ((r + 4 * parity + 4 * ((x // 8) % 2)) % BS) * unit + d % unit
 
 
 def page_rows(page_flat: np.ndarray, D: int, unit: int, parity: int) -> np.ndarray:
