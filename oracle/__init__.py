@@ -54,6 +54,8 @@ def _load():
         lib.ref_rms_norm.argtypes = [P, P, ctypes.c_int, dbl, P]
         lib.ref_rope.restype = None
         lib.ref_rope.argtypes = [P, ctypes.c_int, dbl, dbl, ctypes.c_int, dbl, P]
+        lib.ref_rope_rows.restype = None
+        lib.ref_rope_rows.argtypes = [P, P, i64, ctypes.c_int, dbl, ctypes.c_int, dbl, P]
         lib.ref_kv_cache_write.restype = ctypes.c_int
         lib.ref_kv_cache_write.argtypes = [ctypes.c_int] * 5 + [dbl, ctypes.c_int, dbl, dbl,
                                                                 ctypes.c_int] + [P] * 6 \
@@ -127,6 +129,20 @@ def rope(x: np.ndarray, t: float, theta: float, angles: int = 0, pos_scale: floa
     D = x.shape[-1]
     a = angles if 0 < angles < D // 2 else D // 2
     _load().ref_rope(_p(x), D, float(t), float(theta), int(a), float(pos_scale), _p(y))
+    return y
+
+
+def rope_rows(x: np.ndarray, t: np.ndarray, theta: float, angles: int = 0,
+              pos_scale: float = 1.0) -> np.ndarray:
+    """`rope` of every row x[i] ([N][D]) at its own position t[i]."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    t = np.ascontiguousarray(t, dtype=np.float64)
+    assert x.ndim == 2 and t.shape == (x.shape[0],)
+    D = x.shape[1]
+    a = angles if 0 < angles < D // 2 else D // 2
+    y = np.empty_like(x)
+    _load().ref_rope_rows(_p(x), _p(t), x.shape[0], D, float(theta), int(a), float(pos_scale),
+                          _p(y))
     return y
 
 

@@ -190,6 +190,14 @@ void ref_rope(const double* x, int D, double t, double theta, int angles, double
   }
 }
 
+/* ref_rope applied to n rows x[i*D ..] at positions t[i] (independent rows, in parallel). */
+void ref_rope_rows(const double* x, const double* t, int64_t n, int D, double theta, int angles,
+                   double pos_scale, double* y) {
+  int64_t i;
+#pragma omp parallel for schedule(static)
+  for (i = 0; i < n; ++i) ref_rope(x + i * D, D, t[i], theta, angles, pos_scale, y + i * D);
+}
+
 /* Norm, rotate and scatter the new tokens of every sequence.
  *   q: [T][Hq][D] raw in, written back normalised and rotated (may be NULL);
  *   k, v: [T][Hkv][D] raw (v NULL iff k_eq_v); k and v both NULL: a layer that shares another

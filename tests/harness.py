@@ -7,12 +7,15 @@ write stage is compared separately, element by element, against the oracle's own
 """
 from __future__ import annotations
 
+import dataclasses
+
 import numpy as np
 import torch
 
 import oracle
 import paged_kv_cache_write_amd as ga
 import workloads as wl
+from layout import logical_k, put_k_rows, unit_elems
 
 BF16_MAX_ABS, BF16_MEAN_ABS = 2e-2, 2e-3   # bf16 inputs, fp32 accumulation
 FP32_MAX_ABS = 1e-4
@@ -22,12 +25,12 @@ def dtype_code(spec):
     return oracle.BF16 if spec.dtype == "bf16" else oracle.FP32
 
 
-def params(spec) -> ga.LayerParams:
+def params(spec, kv_norm_w=None) -> ga.LayerParams:
     return ga.layer_params(spec.dtype, spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
                            window=spec.window, scale=spec.scale, softcap=spec.softcap,
                            k_eq_v=spec.k_eq_v, rope_theta=spec.rope_theta, rms_eps=spec.rms_eps,
                            rope_angles=spec.rope_angles, rope_scale=spec.rope_scale,
-                           page_ring=spec.page_ring)
+                           page_ring=spec.page_ring, kv_norm_w=kv_norm_w)
 
 
 def i32(a, device):
@@ -39,11 +42,16 @@ class PagedCase:
 
     def __init__(self, spec: wl.LayerSpec, pb: wl.PagedBatch, seed: int, device="cuda"):
         self.spec, self.pb, self.seed, self.dev = spec, pb, seed, torch.device(device)
-        self.p = params(spec)
         self.kc, self.vc = wl.empty_caches(spec, pb.num_blocks, self.dev)
-        w = wl.norm_weights(spec, seed)
+        exact = spec.k_eq_v == 2  # exact K=V: the layer also has a v norm weight
+        w = wl.norm_weights(dataclasses.replace(spec, k_eq_v=False) if exact else spec, seed)
         self.w_cpu = w
         self.w = [None if x is None else x.to(self.dev) for x in w]
+        self.kvw = None
+        if exact:
+            self.kvw = (self.w[1], self.w[2])
+            self.w = [self.w[0], self.w[1], None]  # the write takes no v norm
+        self.p = params(spec, self.kvw)
         self.bt = i32(pb.block_table, self.dev)
 
     # -- writes -------------------------------------------------------------------------
@@ -159,6 +167,36 @@ def ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     d = np.where(nan_a & nan_b, 0, d)
     d = np.where(nan_a ^ nan_b, np.iinfo(np.int64).max, d)
     return d
+
+
+def exact_kv_reference_caches(spec, kc, block_table, lens, wk, wv):
+    """fp32 K and V caches (the library's fp32 layouts) holding what exact-K=V stored keys C
+    mean: K = RoPE(C) by the oracle's rotation (in double, then fp32) and V = C * w_v / w_k.
+    kc: the stored cache as host bits / fp32; wk, wv: CPU fp32 weights."""
+    D, Hkv = spec.head_dim, spec.num_kv_heads
+    unit = unit_elems(spec.dtype)
+    rows = logical_k(kc, block_table, lens, unit)
+    if spec.dtype == "bf16":
+        rows = (rows.astype(np.uint32) << 16).view(np.float32)
+    blk, r, t = [], [], []
+    for b, L in enumerate(lens):
+        pos = np.arange(int(L))
+        blk.append(block_table[b, pos // wl.BLOCK_SIZE])
+        r.append(pos % wl.BLOCK_SIZE)
+        t.append(pos)
+    blk, r, t = (np.concatenate(x).astype(np.int64) for x in (blk, r, t))
+    X = rows[blk, :, r, :].astype(np.float64)  # [N, Hkv, D]
+    f = spec.rope_scale if spec.rope_scale > 0 else 1.0
+    Kr = oracle.rope_rows(X.reshape(-1, D), np.repeat(t, Hkv), float(np.float32(spec.rope_theta)),
+                          spec.rope_angles, float(np.float32(f))).reshape(-1, Hkv, D)
+    nb = kc.shape[0]
+    K = np.full((nb, Hkv, wl.BLOCK_SIZE, D), np.nan, np.float32)
+    V = np.full((nb, Hkv, D, wl.BLOCK_SIZE), np.nan, np.float32)
+    for g in range(Hkv):
+        put_k_rows(K, blk, g, t, Kr[:, g].astype(np.float32), 4)
+    ratio = wv.double().numpy() / wk.double().numpy()
+    V[blk[:, None], np.arange(Hkv)[None, :], :, r[:, None]] = (X * ratio).astype(np.float32)
+    return K, V
 
 
 def compact_pages(case: PagedCase, seqs, lens):

@@ -20,8 +20,7 @@ import torch
 import oracle
 import paged_kv_cache_write_amd as ga
 import workloads as wl
-from harness import assert_attn_close, i32
-from layout import logical_k, put_k_rows
+from harness import assert_attn_close, exact_kv_reference_caches, i32
 
 pytestmark = pytest.mark.gpu
 
@@ -85,32 +84,12 @@ class ExactCase:
     def oracle_stored(self, q_dev, cu, cl, scale):
         """Attention over what the stored keys C mean: K = RoPE(C), V = C * w_v / w_k."""
         s = self.spec
-        D, Hkv = s.head_dim, s.num_kv_heads
-        bt, lens = self.pb.block_table, self.pb.context_lens
-        unit = 8 if s.dtype == "bf16" else 4
-        kc = wl.to_numpy_bits(self.kc)
-        rows = logical_k(kc, bt, lens, unit)
-        if s.dtype == "bf16":
-            rows = (rows.astype(np.uint32) << 16).view(np.float32)
-        ratio = self.w[2].double().numpy() / self.w[1].double().numpy()
-        nb = kc.shape[0]
-        K = np.full((nb, Hkv, BS, D), np.nan, np.float32)
-        V = np.full((nb, Hkv, D, BS), np.nan, np.float32)
-        f = s.rope_scale if s.rope_scale > 0 else 1.0
-        for b, L in enumerate(lens):
-            for t in range(int(L)):
-                blk, r = int(bt[b, t // BS]), t % BS
-                for g in range(Hkv):
-                    x = rows[blk, g, r].astype(np.float64)
-                    kr = oracle.rope(x, float(t), float(np.float32(s.rope_theta)), s.rope_angles,
-                                     float(np.float32(f)))
-                    put_k_rows(K, np.array([blk]), g, np.array([t]), kr[None].astype(np.float32),
-                               4)
-                    V[blk, g, :, r] = (x * ratio).astype(np.float32)
-        q32 = q_dev.float().cpu().numpy()
-        return oracle.attention(oracle.FP32, s.num_q_heads, Hkv, D, s.window,
-                                float(np.float32(scale)), float(np.float32(s.softcap)), 0,
-                                np.ascontiguousarray(q32), cu, K, V, bt, cl)
+        K, V = exact_kv_reference_caches(s, wl.to_numpy_bits(self.kc), self.pb.block_table,
+                                         self.pb.context_lens, self.w[1], self.w[2])
+        q32 = np.ascontiguousarray(q_dev.float().cpu().numpy())
+        return oracle.attention(oracle.FP32, s.num_q_heads, s.num_kv_heads, s.head_dim, s.window,
+                                float(np.float32(scale)), float(np.float32(s.softcap)), 0, q32,
+                                cu, K, V, self.pb.block_table, cl)
 
 
 CASES = [  # D, Hq, Hkv, theta, rope_angles, rope_scale, window

@@ -4,14 +4,16 @@ Small workloads are compared with the oracle on every output; the large ones on 
 sequences / query rows that the oracle computes one by one (the sample is stated per test),
 plus properties that hold at any size (tail-only reads of sliding decode).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import workloads as wl
-from harness import (PagedCase, assert_attn_close, compact_pages, dtype_code, oracle_write,
-                     ulp_distance)
+from harness import (PagedCase, assert_attn_close, compact_pages, dtype_code,
+                     exact_kv_reference_caches, oracle_write, ulp_distance)
 
 pytestmark = pytest.mark.gpu
 
@@ -205,3 +207,48 @@ def test_chunk_write_matches_oracle_on_sampled_tokens():
     assert ulp_distance(vc1[pages], vc0[pages]).max() <= 1
     assert ulp_distance(wl.to_numpy_bits(qd)[sel_tok], qh).max() <= 1
 
+
+
+def test_kv_shared_decode_bf16_exact_form_full():
+    """The K=V decode workload (16 x ~32k, head size 512) in the exact K=V form the bench times
+    (unrotated keys, 64 rotated pairs, a v norm weight): 3 sampled sequences vs the oracle over
+    the stored bytes (K = RoPE(C), V = C * w_v / w_k)."""
+    specs, pb = wl.workload("kv_shared_decode_bf16")
+    spec = dataclasses.replace(specs[0], k_eq_v=2, rope_angles=64)
+    case = PagedCase(spec, pb, 4)
+    lens = pb.context_lens
+    _fill_past(case, lens, np.ones_like(lens), 400, chunk=8192)
+    q, k, v, qd, cu, cl = case.write(lens, np.ones_like(lens), 4)
+    out = case.decode(qd, cl)
+    torch.cuda.synchronize()
+    seqs = [int(np.argmin(lens)), int(np.argmax(lens)), 7]
+    kc, _, nbt = compact_pages(case, seqs, lens)
+    K, V = exact_kv_reference_caches(spec, kc, nbt, lens[seqs], case.w_cpu[1], case.w_cpu[2])
+    q32 = np.ascontiguousarray(qd[seqs].float().cpu().numpy())
+    ref = oracle.attn_decode(oracle.FP32, 32, 4, 512, 0, 1.0, 0.0, 0, q32, K, V, nbt,
+                             lens[seqs])
+    mx, mean = assert_attn_close(out[seqs], ref, "bf16", what="exact K=V decode")
+    print(f"kv_shared_decode exact (3 of 16 seqs): max {mx:.3e} mean {mean:.3e}")
+
+
+def test_chunked_prefill_global_layer_exact_form_full():
+    """The chunked-prefill global layer (4 x 2048 after 6144, D 512, 32/4 heads) in the exact
+    K=V form the bench times: the first and last 4 rows and 4 random rows per sequence vs the
+    oracle over the stored bytes."""
+    specs, pb = wl.workload("chunked_prefill_bf16")
+    spec = dataclasses.replace(specs[5], k_eq_v=2, rope_angles=64)
+    case = PagedCase(spec, pb, 5)
+    lens, news = pb.context_lens, pb.n_new
+    _fill_past(case, lens, news, 500)
+    q, k, v, qd, cu, cl = case.write(lens, news, 5)
+    out = case.prefill(qd, cu, cl)
+    torch.cuda.synchronize()
+    rows = _sample_rows(cu, 0, lens - news, 4, 5, edge=4)
+    kc, _ = case.host_caches()
+    K, V = exact_kv_reference_caches(spec, kc, pb.block_table, lens, case.w_cpu[1],
+                                     case.w_cpu[2])
+    q32 = np.ascontiguousarray(qd.float().cpu().numpy())
+    ref = oracle.attention(oracle.FP32, 32, 4, 512, 0, 1.0, 0.0, 0, q32, cu, K, V,
+                           pb.block_table, cl, rows=rows)
+    mx, mean = assert_attn_close(out, ref, "bf16", rows=rows, what="prefill global exact")
+    print(f"chunked_prefill global exact ({len(rows)} rows): max {mx:.3e} mean {mean:.3e}")
