@@ -43,6 +43,7 @@ struct KvWriteArgs {
   int32_t Hq, Hkv, nslots, has_q, k_eq_v;
   int32_t slots_per_wg, groups;  // head slots per workgroup; workgroups per token
   double theta, eps, pos_scale;
+  double log2_theta;  // log2(theta), formed on the host
   int32_t rope_angles;
   int32_t has_kv;  // 0: q only (a layer that reads another layer's cache)
   int32_t ring;    // block-table rows are rings of max_blocks pages
@@ -64,6 +65,28 @@ struct Elem<uint16_t> {
     ((uint16_t*)p)[i] = f64_to_bf16(x);
   }
 };
+
+// Store C consecutive elements (index i, a multiple of C, so the run is aligned) with one
+// store instruction: a lane's C elements of a half-row are consecutive in q and, inside one
+// 16-byte unit, in the K page.
+template <typename T, int C>
+__device__ __forceinline__ void store_run(void* p, int64_t i, const double (&x)[C]) {
+  if constexpr (sizeof(T) == 2 && C == 2) {
+    const uint32_t w = (uint32_t)f64_to_bf16(x[0]) | ((uint32_t)f64_to_bf16(x[1]) << 16);
+    *(uint32_t*)((uint16_t*)p + i) = w;
+  } else if constexpr (sizeof(T) == 2 && C == 4) {
+    const uint64_t w = (uint64_t)f64_to_bf16(x[0]) | ((uint64_t)f64_to_bf16(x[1]) << 16) |
+                       ((uint64_t)f64_to_bf16(x[2]) << 32) | ((uint64_t)f64_to_bf16(x[3]) << 48);
+    *(uint64_t*)((uint16_t*)p + i) = w;
+  } else if constexpr (sizeof(T) == 4 && C == 2) {
+    *(float2*)((float*)p + i) = make_float2((float)x[0], (float)x[1]);
+  } else if constexpr (sizeof(T) == 4 && C == 4) {
+    *(float4*)((float*)p + i) = make_float4((float)x[0], (float)x[1], (float)x[2], (float)x[3]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < C; ++e) Elem<T>::store(p, i + e, x[e]);
+  }
+}
 
 constexpr int kRowsInFlight = 4;  // (token, head) rows whose loads one wave keeps in flight
 
@@ -103,8 +126,15 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
   constexpr int H = D / 2;
   __shared__ double cos_t[H], sin_t[H];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t tok = blockIdx.x / a.groups;
-  const int group = (int)(blockIdx.x - tok * a.groups);
+  // Workgroup ids are dealt to the 8 XCDs round robin; remap them so that each XCD takes a
+  // contiguous range of (token, slot group) items.  Consecutive tokens of a sequence share
+  // cache pages (16 rows of every 256-byte K column run and every 32-byte V row), so their
+  // partial-line stores then meet in one L2 and leave it as whole lines.  The grid is a
+  // multiple of 8, so the remap is a bijection; ids past the work return.
+  const int64_t per_xcd = gridDim.x / 8;
+  const int64_t item = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  const int64_t tok = item / a.groups;
+  const int group = (int)(item - tok * a.groups);
   if (tok >= a.total_tokens) return;
 
   // this wave's first kRowsInFlight rows are loaded before anything else: they depend only on
@@ -161,7 +191,8 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
     for (int k = threadIdx.x; k < H; k += 256) {
       double sn = 0.0, cs = 1.0;
       if (k < a.rope_angles) {
-        const double omega = 1.0 / pow(a.theta, (2.0 * k) / (double)D);
+        // theta^(-2k/D) as exp2 of a product: within a few ulp of the power, like it
+        const double omega = exp2(-((2.0 * k) / (double)D) * a.log2_theta);
         sincos(tp * omega, &sn, &cs);
       }
       cos_t[k] = cs;
@@ -210,19 +241,12 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
         }
       }
       if (r.kind == 0) {
-#pragma unroll
-        for (int i = 0; i < C; ++i) {
-          Elem<T>::store(a.q, r.base + lane * C + i, x1[i]);
-          Elem<T>::store(a.q, r.base + H + lane * C + i, x2[i]);
-        }
+        store_run<T, C>(a.q, r.base + lane * C, x1);
+        store_run<T, C>(a.q, r.base + H + lane * C, x2);
       } else if (r.kind == 1) {
         const int64_t pg = (blk * a.Hkv + r.h) * (int64_t)D * kPage;
-#pragma unroll
-        for (int i = 0; i < C; ++i) {
-          Elem<T>::store(a.kc, pg + k_page_elem<sizeof(T)>((int)off, lane * C + i, page), x1[i]);
-          Elem<T>::store(a.kc, pg + k_page_elem<sizeof(T)>((int)off, H + lane * C + i, page),
-                         x2[i]);
-        }
+        store_run<T, C>(a.kc, pg + k_page_elem<sizeof(T)>((int)off, lane * C, page), x1);
+        store_run<T, C>(a.kc, pg + k_page_elem<sizeof(T)>((int)off, H + lane * C, page), x2);
       } else {
         const int64_t pg = (blk * a.Hkv + r.h) * (int64_t)D * kPage;
 #pragma unroll
@@ -246,7 +270,7 @@ hipError_t launch_t(KvWriteArgs a, hipStream_t s) {
   per_wave = per_wave < 1 ? 1 : (per_wave > max_per_wave ? max_per_wave : per_wave);
   a.slots_per_wg = (int)(4 * per_wave);
   a.groups = (a.nslots + a.slots_per_wg - 1) / a.slots_per_wg;
-  const int64_t blocks = (int64_t)a.total_tokens * a.groups;
+  const int64_t blocks = ((int64_t)a.total_tokens * a.groups + 7) / 8 * 8;  // whole XCD rounds
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((kv_write_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
@@ -269,6 +293,7 @@ hipError_t launch_kv_write(const KvWriteLaunch& L, hipStream_t s) {
   a.ring = L.ring;
   a.nslots = (a.has_q ? L.Hq : 0) + (a.has_kv ? L.Hkv + (L.k_eq_v ? 0 : L.Hkv) : 0);
   a.theta = (double)L.rope_theta;
+  a.log2_theta = a.theta > 0.0 ? log2(a.theta) : 0.0;
   a.rope_angles = L.rope_angles;
 
   a.pos_scale = (double)L.rope_scale;
