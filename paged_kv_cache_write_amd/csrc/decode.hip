@@ -333,8 +333,10 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(AttnArgs a) {
 }
 
 // Merge the pieces of one (sequence, query head): out = sum 2^(m_i-M) o_i / sum 2^(m_i-M) l_i.
-// Stage 1 turns every piece's (m, l) into a weight in LDS; stage 2 splits the D/4 float4
-// columns x pieces over the 256 threads so that many loads are in flight, then sums groups.
+// The D/4 float4 columns x pieces are split over the 256 threads.  Only the prefix array is
+// read before anything else: the (m, l) pairs and the first kPre partial rows of each thread
+// are then loaded together (their addresses do not depend on the weights), so the merge waits
+// on two round trips to memory, not four.
 __device__ __forceinline__ float block_reduce(float v, bool is_max, float* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -355,6 +357,7 @@ template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
   constexpr int C4 = D / 4;     // float4 columns
   constexpr int NG = 256 / C4;  // piece groups
+  constexpr int kPre = 8;       // partial rows prefetched per thread
   __shared__ float wts[kMaxWorkers + 1];
   __shared__ float red[4];
   __shared__ float4_t part[256];
@@ -373,11 +376,28 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
   const int64_t w0 = start / per, w1 = (start + npg - 1) / per;
   const int ns = (int)(w1 - w0 + 1);
   const int64_t row0 = (w0 + (int64_t)b * a.Hkv + g) * G + hh;  // row of piece i: row0 + i*G
-  float mloc = -INFINITY;
-  for (int i = t; i < ns; i += 256) mloc = fmaxf(mloc, a.ws_ml[(row0 + (int64_t)i * G) * 2]);
+  const int c = t % C4, gi = t / C4;
+  const float* ocol = a.ws_o + row0 * D + 4 * c;
+  const int64_t ostep = (int64_t)G * D;
+
+  float4_t pre[kPre];
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) {
+    const int i = gi + k * NG;
+    pre[k] = i < ns ? *(const float4_t*)(ocol + i * ostep) : float4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  float2 ml0 = make_float2(-INFINITY, 0.f);
+  if (t < ns) ml0 = *(const float2*)(a.ws_ml + (row0 + (int64_t)t * G) * 2);
+  float mloc = ml0.x;
+  for (int i = t + 256; i < ns; i += 256) mloc = fmaxf(mloc, a.ws_ml[(row0 + (int64_t)i * G) * 2]);
   const float M = block_reduce(mloc, true, red);
   float lloc = 0.f;
-  for (int i = t; i < ns; i += 256) {
+  if (t < ns) {
+    const float e = fast_exp2(ml0.x - M);
+    wts[t] = e;
+    lloc = e * ml0.y;
+  }
+  for (int i = t + 256; i < ns; i += 256) {
     const float2 ml = *(const float2*)(a.ws_ml + (row0 + (int64_t)i * G) * 2);
     const float e = fast_exp2(ml.x - M);
     wts[i] = e;
@@ -385,13 +405,14 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
   }
   const float Lsum = block_reduce(lloc, false, red);  // its barrier also publishes wts
   const float inv = 1.0f / Lsum;
-  const int c = t % C4, gi = t / C4;
   float4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int i = gi; i < ns; i += NG) {
-    const float4_t v = *(const float4_t*)(a.ws_o + (row0 + (int64_t)i * G) * D + 4 * c);
-    acc += wts[i] * v;
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) {
+    const int i = gi + k * NG;
+    if (i < ns) acc += wts[i] * pre[k];
   }
+#pragma unroll 4
+  for (int i = gi + kPre * NG; i < ns; i += NG) acc += wts[i] * *(const float4_t*)(ocol + i * ostep);
   part[t] = acc;
   __syncthreads();
   if (gi == 0) {
