@@ -221,6 +221,28 @@ const char* ga_status_string(ga_status s);
 /* Thread-local reason of the most recent failing call on this thread ("" if none). */
 const char* ga_last_error(void);
 
+/* In-kernel metadata checks (the scope table's boundary sketch: a debug build that also checks
+ * the device-resident metadata in the kernels and records what it finds in a device word).
+ * libgemma_attn_debug.so is built with GA_DEBUG_BOUNDS: its kernels check every block id they
+ * read, the lengths against cu_seqlens and the host bounds, and the owner of every new token,
+ * and set bits of a per-device word; the results and the clamps that keep every access in
+ * bounds are the same as in the regular build.  This call waits for the device, returns the
+ * OR of the bits set since the last call into *flags (HOST) and clears them.
+ *   GA_DEBUG_BLOCK_ID  a block id the call read lies outside [0, num_blocks) (clamped, or for
+ *                      the write: the token is skipped)
+ *   GA_DEBUG_LENGTH    lengths inconsistent: L_b < n_b, a decode length < 1, cu_seqlens out of
+ *                      order or past total_q / max_q_len
+ *   GA_DEBUG_BOUND     a length beyond the host bound (max_context_len; the pages of a
+ *                      block-table row)
+ *   GA_DEBUG_OWNER     a new token that no sequence of cu_seqlens owns
+ * The regular library returns GA_ERR_UNSUPPORTED (and *flags = 0).  GA_ERR_HIP: the word could
+ * not be read.  Calls running while this one reads race with its clear. */
+#define GA_DEBUG_BLOCK_ID 1u
+#define GA_DEBUG_LENGTH 2u
+#define GA_DEBUG_BOUND 4u
+#define GA_DEBUG_OWNER 8u
+ga_status ga_debug_take_error(uint32_t* flags);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,6 +16,8 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "lib", "libgemma_attn.so")
+# the same library built with the in-kernel metadata checks (GA_DEBUG_BOUNDS)
+DEBUG_LIB_PATH = os.path.join(_PKG, "lib", "libgemma_attn_debug.so")
 
 GA_FP32, GA_BF16 = 0, 1
 BLOCK_SIZE = 16
@@ -95,8 +97,32 @@ def load_library():
     lib.ga_status_string.argtypes = [ctypes.c_int]
     lib.ga_last_error.restype = ctypes.c_char_p
     lib.ga_last_error.argtypes = []
+    lib.ga_debug_take_error.restype = ctypes.c_int
+    lib.ga_debug_take_error.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
     _lib = lib
     return lib
+
+
+def select_library(path: str) -> str:
+    """Make the calls of this module go to the library at `path` (e.g. DEBUG_LIB_PATH);
+    returns the previous path.  Loaded libraries stay loaded, so switching back is cheap."""
+    global LIB_PATH, _lib
+    prev = LIB_PATH
+    LIB_PATH, _lib = path, None
+    load_library()
+    return prev
+
+
+# bits of debug_take_error (GA_DEBUG_* of the header)
+DEBUG_BLOCK_ID, DEBUG_LENGTH, DEBUG_BOUND, DEBUG_OWNER = 1, 2, 4, 8
+
+
+def debug_take_error() -> int:
+    """The in-kernel metadata-check bits set since the last call (debug library only; waits for
+    the device and clears them).  The regular library raises GAError (GA_ERR_UNSUPPORTED)."""
+    v = ctypes.c_uint32(0)
+    _raise_on(load_library().ga_debug_take_error(ctypes.byref(v)))
+    return int(v.value)
 
 
 def _raise_on(status: int):
@@ -213,4 +239,5 @@ def check_metadata_host(p: LayerParams, cu_seqlens, context_lens, block_table, n
 
 __all__ = ["LayerParams", "layer_params", "kv_cache_write", "attn_decode", "attn_prefill",
            "decode_workspace_bytes", "decode_workspace", "check_metadata_host", "GAError",
-           "load_library", "LIB_PATH", "GA_FP32", "GA_BF16", "BLOCK_SIZE"]
+           "load_library", "LIB_PATH", "DEBUG_LIB_PATH", "select_library", "debug_take_error",
+           "DEBUG_BLOCK_ID", "DEBUG_LENGTH", "DEBUG_BOUND", "DEBUG_OWNER", "GA_FP32", "GA_BF16", "BLOCK_SIZE"]

@@ -13,8 +13,11 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build", "obj")
+OBJ_DEBUG = os.path.join(ROOT, "_build", "obj_debug")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIB_DIR, "libgemma_attn.so")
+# the same sources with the in-kernel metadata checks (GA_DEBUG_BOUNDS)
+LIB_DEBUG = os.path.join(LIB_DIR, "libgemma_attn_debug.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "kv_write.hip", "attention.hip", "decode.hip", "prefill.hip"]
@@ -26,30 +29,40 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", out]
+def _compile(job) -> str:
+    src, debug = job
+    out = os.path.join(OBJ_DEBUG if debug else OBJ, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC] + FLAGS + (["-DGA_DEBUG_BOUNDS"] if debug else []) + \
+        ["-c", os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+        raise RuntimeError(f"hipcc failed on {src}{' (debug)' if debug else ''}:\n{r.stderr}")
     return out
 
 
-def build(verbose: bool = False) -> str:
-    """Compile and link; always rebuilds.  Returns the path of the shared library."""
-    os.makedirs(OBJ, exist_ok=True)
-    os.makedirs(LIB_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs + \
         ["-Wl,-rpath,/opt/rocm/lib"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile and link both libraries (regular and GA_DEBUG_BOUNDS); always rebuilds.
+    Returns the path of the regular shared library."""
+    os.makedirs(OBJ, exist_ok=True)
+    os.makedirs(OBJ_DEBUG, exist_ok=True)
+    os.makedirs(LIB_DIR, exist_ok=True)
+    jobs = [(src, False) for src in SOURCES] + [(src, True) for src in SOURCES]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as ex:
+        objs = list(ex.map(_compile, jobs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], LIB_DEBUG)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", LIB_DEBUG)
     return LIB
 
 

@@ -380,4 +380,23 @@ ga_status ga_check_metadata_host(const ga_layer_params* p, const int32_t* cu_seq
   return ok();
 }
 
+static_assert(ga::kDbgBlockId == GA_DEBUG_BLOCK_ID && ga::kDbgLength == GA_DEBUG_LENGTH &&
+                  ga::kDbgBound == GA_DEBUG_BOUND && ga::kDbgOwner == GA_DEBUG_OWNER,
+              "check bits of the header and of the kernels");
+
+ga_status ga_debug_take_error(uint32_t* flags) {
+  if (!flags) return fail(GA_ERR_INVALID_ARG, "flags is NULL");
+  *flags = 0;
+#ifdef GA_DEBUG_BOUNDS
+  const uint32_t w = ga::debug_take_kv_write() | ga::debug_take_decode() |
+                     ga::debug_take_prefill() | ga::debug_take_attention();
+  if (w & ga::kDbgReadFailed) return fail(GA_ERR_HIP, "reading the check words failed");
+  *flags = w;
+  return ok();
+#else
+  return fail(GA_ERR_UNSUPPORTED, "in-kernel metadata checks are only in the GA_DEBUG_BOUNDS "
+                                  "build");
+#endif
+}
+
 }  // extern "C"

@@ -45,10 +45,14 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* q, const int
     b = lo; i = rq - cu[b]; n = cu[b + 1] - cu[b];
   }
   int L = ctx[b];
-  if (decode && L > max_len) L = max_len;
+  if (decode && L > max_len) {
+    debug_flag(kDbgBound);
+    L = max_len;
+  }
   const int t = L - n + i;
   float* dst = out + ((int64_t)rq * Hq + h) * D + lane * C;
   if (t < 0 || L < 1) {
+    debug_flag(kDbgLength);
 #pragma unroll
     for (int e = 0; e < C; ++e) dst[e] = 0.f;
     return;
@@ -77,7 +81,10 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* q, const int
   float m = -INFINITY, l = 0.f;
   for (int key = lo; key <= t; ++key) {
     const int page = key / kPage;
-    if (!ring && page >= max_blocks) break;
+    if (!ring && page >= max_blocks) {
+      debug_flag(kDbgBound);
+      break;
+    }
     const int64_t blk =
         clamp_blk(bt[(int64_t)b * max_blocks + bt_col(page, max_blocks, ring)], num_blocks);
     const int off = key - page * kPage;
@@ -141,6 +148,8 @@ hipError_t launch_f32_t(const AttnLaunch& L, bool decode, hipStream_t s) {
 }
 
 }  // namespace
+
+GA_DEBUG_TAKE_DEFINE(debug_take_attention)
 
 AttnArgs make_attn_args(const AttnLaunch& L) {
   AttnArgs a;

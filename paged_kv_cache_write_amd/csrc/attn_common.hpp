@@ -92,7 +92,11 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 __device__ __forceinline__ int64_t clamp_blk(int64_t blk, int64_t nb) {
-  return blk < 0 ? 0 : (blk >= nb ? nb - 1 : blk);
+  if (blk < 0 || blk >= nb) {
+    debug_flag(kDbgBlockId);
+    return blk < 0 ? 0 : nb - 1;
+  }
+  return blk;
 }
 
 struct AttnArgs {
@@ -185,8 +189,12 @@ __device__ __forceinline__ double rope_rho(const double rho0, const double rho_s
 __device__ __forceinline__ void decode_range(const AttnArgs& a, int b, int& L, int& lo, int& p0,
                                              int& npg) {
   L = a.ctx[b];
-  L = L > a.max_ctx ? a.max_ctx : L;
+  if (L > a.max_ctx) {
+    debug_flag(kDbgBound);
+    L = a.max_ctx;
+  }
   if (L < 1) {
+    debug_flag(kDbgLength);
     L = 0; lo = 0; p0 = 0; npg = 0;
     return;
   }

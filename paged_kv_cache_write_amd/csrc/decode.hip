@@ -485,6 +485,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
+GA_DEBUG_TAKE_DEFINE(debug_take_decode)
+
 DecodePlan plan_decode(int D, int Hq, int Hkv, int window, int batch, int max_context_len,
                        bool bf16) {
   DecodePlan p{0, 0, 0, 0, 0, 0};

@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.hpp"
+
 namespace ga {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
@@ -100,6 +102,34 @@ __device__ __forceinline__ int64_t k_page_elem(int r, int d, int64_t lp) {
 __device__ __forceinline__ int bt_col(int lp, int max_blocks, int ring) {
   return ring ? (int)((unsigned)lp % (unsigned)max_blocks) : lp;
 }
+
+// ------------------------------------------------------------------------ debug checks ------
+// Built with GA_DEBUG_BOUNDS, the kernels also check the device-resident metadata they read and
+// record what they find as bits of a device word, one per source file (the kernels are compiled
+// file by file, without device linking); ga_debug_take_error reads and clears the words.  The
+// regular build compiles no check.  Either way every kernel keeps its own clamps, so bad
+// metadata never leads to an access outside the buffers it was given.
+// (the bits are the kDbg* constants of launch.hpp)
+#ifdef GA_DEBUG_BOUNDS
+static __device__ uint32_t g_debug_word;
+__device__ __forceinline__ void debug_flag(uint32_t bits) { atomicOr(&g_debug_word, bits); }
+// host: the word of this source file on the current device, cleared (synchronous)
+#define GA_DEBUG_TAKE_DEFINE(fn)                                                             \
+  uint32_t fn() {                                                                            \
+    uint32_t v = 0;                                                                          \
+    const uint32_t zero = 0;                                                                 \
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_debug_word), sizeof(v), 0,                      \
+                            hipMemcpyDeviceToHost) != hipSuccess ||                          \
+        hipMemcpyToSymbol(HIP_SYMBOL(g_debug_word), &zero, sizeof(zero), 0,                  \
+                          hipMemcpyHostToDevice) != hipSuccess)                              \
+      return kDbgReadFailed;                                                                 \
+    return v;                                                                                \
+  }
+#else
+__device__ __forceinline__ void debug_flag(uint32_t) {}
+#define GA_DEBUG_TAKE_DEFINE(fn) \
+  uint32_t fn() { return 0u; }
+#endif
 
 // ------------------------------------------------------------------------ MFMA --------------
 

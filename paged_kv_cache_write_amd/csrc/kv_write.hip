@@ -170,13 +170,22 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
   }
   __syncthreads();
   const int b = owner;
-  if (b < 0) return;  // tok beyond cu[batch]: nothing owns it
+  if (b < 0) {  // no sequence owns tok (cu_seqlens inconsistent)
+    debug_flag(kDbgOwner);
+    return;
+  }
   const int64_t t = own_t;
   const int64_t page = t >> 4;
-  if (t < 0) return;  // inconsistent metadata: write nothing
+  if (t < 0) {  // inconsistent metadata (n_b > L_b): write nothing
+    debug_flag(kDbgLength);
+    return;
+  }
   int64_t blk = 0;
   if (a.has_kv) {
-    if (!a.ring && page >= a.max_blocks) return;  // (all the exits are workgroup-uniform)
+    if (!a.ring && page >= a.max_blocks) {  // (all the exits are workgroup-uniform)
+      debug_flag(kDbgBound);
+      return;
+    }
     // the block id is checked after the rotation table, which its load latency overlaps
     blk = a.bt[(int64_t)b * a.max_blocks + bt_col((int)page, a.max_blocks, a.ring)];
   }
@@ -199,7 +208,10 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
       sin_t[k] = sn;
     }
   }
-  if (a.has_kv && (blk < 0 || blk >= a.num_blocks)) return;  // no slot to write: nothing
+  if (a.has_kv && (blk < 0 || blk >= a.num_blocks)) {  // no slot to write: nothing
+    debug_flag(kDbgBlockId);
+    return;
+  }
   __syncthreads();
 
   // the rows of this wave, kRowsInFlight at a time: all their loads are issued before the
@@ -277,6 +289,8 @@ hipError_t launch_t(KvWriteArgs a, hipStream_t s) {
 }
 
 }  // namespace
+
+GA_DEBUG_TAKE_DEFINE(debug_take_kv_write)
 
 hipError_t launch_kv_write(const KvWriteLaunch& L, hipStream_t s) {
   KvWriteArgs a;

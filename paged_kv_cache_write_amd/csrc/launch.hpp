@@ -71,4 +71,20 @@ hipError_t launch_decode(const AttnLaunch& a, const DecodePlan& plan, hipStream_
 hipError_t launch_prefill(const AttnLaunch& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnLaunch& a, bool decode, hipStream_t s);
 
+// Debug build (GA_DEBUG_BOUNDS): bits of the in-kernel metadata checks.
+constexpr uint32_t kDbgBlockId = 1u;  // a block-table entry the call reads is outside [0, nb)
+constexpr uint32_t kDbgLength = 2u;   // lengths inconsistent (L_b < n_b, decode L_b < 1, cu out
+                                      // of order or past its end)
+constexpr uint32_t kDbgBound = 4u;    // a context beyond the host bound (max_context_len, the
+                                      // pages of a table row)
+constexpr uint32_t kDbgOwner = 8u;    // a new token that no sequence of cu_seqlens owns
+constexpr uint32_t kDbgReadFailed = 0x80000000u;  // the word could not be read
+
+// The metadata-check word of each kernel file on the current device, read and cleared (0 in
+// the regular build; kDbgReadFailed if a word could not be read).
+uint32_t debug_take_kv_write();
+uint32_t debug_take_decode();
+uint32_t debug_take_prefill();
+uint32_t debug_take_attention();
+
 }  // namespace ga

@@ -190,11 +190,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
   const int G = a.G, W = a.window;
   const int q0 = a.cu[b];
   int n = a.cu[b + 1] - q0;
+  if (n > a.max_q_len || n > a.total_q - q0 || n < 0 || q0 < 0) debug_flag(kDbgLength);
   n = n > a.max_q_len ? a.max_q_len : n;
   n = n > a.total_q - q0 ? a.total_q - q0 : n;
   int L = a.ctx[b];
+  if (L > a.max_ctx) debug_flag(kDbgBound);
   L = L > a.max_ctx ? a.max_ctx : L;
   const int past = L - n;
+  if (past < 0) debug_flag(kDbgLength);
   const int row0 = rt * kRowsPerWg;
   if (q0 < 0 || n <= 0 || past < 0 || row0 >= n * G) return;  // uniform over the workgroup
 
@@ -614,6 +617,8 @@ hipError_t by_flags(const AttnArgs& a, bool cap, int kv_mode, hipStream_t s) {
 }
 
 }  // namespace
+
+GA_DEBUG_TAKE_DEFINE(debug_take_prefill)
 
 hipError_t launch_prefill(const AttnLaunch& L, hipStream_t s) {
   if (L.batch == 0 || L.total_q == 0) return hipSuccess;

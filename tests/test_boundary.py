@@ -31,6 +31,24 @@ def test_library_exports_every_declared_function():
         assert hasattr(lib, n), n
 
 
+def test_debug_library_exports_every_declared_function():
+    lib = ctypes.CDLL(ga.DEBUG_LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert "ga_debug_take_error" in declared_functions()
+
+
+def test_debug_take_error_outside_the_debug_build():
+    # the regular library has no in-kernel checks: it says so without touching the device
+    with pytest.raises(ga.GAError) as e:
+        ga.debug_take_error()
+    assert e.value.status == 2 and "GA_DEBUG_BOUNDS" in str(e.value)
+    dbg = ctypes.CDLL(ga.DEBUG_LIB_PATH)
+    dbg.ga_debug_take_error.restype = ctypes.c_int
+    dbg.ga_debug_take_error.argtypes = [ctypes.c_void_p]
+    assert dbg.ga_debug_take_error(None) == 1  # NULL flags: invalid argument
+
+
 def good(**kw):
     d = dict(dtype="bf16", num_q_heads=8, num_kv_heads=4, head_dim=256, window=0, scale=1.0,
              softcap=0.0, k_eq_v=False, rope_theta=1e4, rms_eps=1e-6)
