@@ -256,15 +256,22 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(AttnArgs a) {
   const int G = a.G, Hkv = a.Hkv, B = a.batch;
   uint16_t* lds = (uint16_t*)smem_raw + (KEQV ? wave * KeqvLds<D>::kElems : 0);
 
-  // total visible pages over the batch (and the prefix array, written once by worker 0)
+  // total visible pages over the batch (and the prefix array, written once by worker 0).  When
+  // the batch fits one wave (B <= 64), lane s keeps sequence s's range and inclusive prefix, so
+  // the rest of the set-up reads them with readlane instead of loading the lengths again
+  const bool one_pass = B <= kWave;
+  int rL = 0, rlo = 0, rp0 = 0, rnpg = 0, rincl = 0;
   int64_t total = 0;
   for (int c0 = 0; c0 < B; c0 += 64) {
-    int L, lo, p0, npg = 0;
+    int L = 0, lo = 0, p0 = 0, npg = 0;
     if (c0 + lane < B) decode_range(a, c0 + lane, L, lo, p0, npg);
     const int incl = wave_incl_scan(npg);
     if (worker == 0) {
       if (c0 == 0 && lane == 0) a.ws_pref[0] = 0;
       if (c0 + lane < B) a.ws_pref[c0 + lane + 1] = (int)total + incl;
+    }
+    if (c0 == 0) {
+      rL = L; rlo = lo; rp0 = p0; rnpg = npg; rincl = incl;
     }
     total += __builtin_amdgcn_readlane(incl, 63);
   }
@@ -278,19 +285,37 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(AttnArgs a) {
   // the sequence holding unit u0: first b with Hkv * prefix(b + 1) > u0
   int b = 0;
   int64_t pref = 0;
-  for (int c0 = 0; c0 < B; c0 += 64) {
-    int L, lo, p0, npg = 0;
-    if (c0 + lane < B) decode_range(a, c0 + lane, L, lo, p0, npg);
-    const int incl = wave_incl_scan(npg);
-    const uint64_t hit = __ballot((pref + incl) * Hkv > u0 && c0 + lane < B);
-    if (hit) {
-      const int f = __builtin_ctzll(hit);
-      b = c0 + f;
-      pref += __builtin_amdgcn_readlane(incl - npg, f);
-      break;
+  if (one_pass) {
+    const uint64_t hit = __ballot((int64_t)rincl * Hkv > u0 && lane < B);
+    if (!hit) return;  // cannot happen: u0 < total
+    b = __builtin_ctzll(hit);
+    pref = __builtin_amdgcn_readlane(rincl - rnpg, b);
+  } else {
+    for (int c0 = 0; c0 < B; c0 += 64) {
+      int L, lo, p0, npg = 0;
+      if (c0 + lane < B) decode_range(a, c0 + lane, L, lo, p0, npg);
+      const int incl = wave_incl_scan(npg);
+      const uint64_t hit = __ballot((pref + incl) * Hkv > u0 && c0 + lane < B);
+      if (hit) {
+        const int f = __builtin_ctzll(hit);
+        b = c0 + f;
+        pref += __builtin_amdgcn_readlane(incl - npg, f);
+        break;
+      }
+      pref += __builtin_amdgcn_readlane(incl, 63);
     }
-    pref += __builtin_amdgcn_readlane(incl, 63);
   }
+  // range of sequence bb (wave-uniform)
+  auto seq_range = [&](int bb, int& L, int& lo, int& p0, int& npg) {
+    if (one_pass) {
+      L = __builtin_amdgcn_readlane(rL, bb);
+      lo = __builtin_amdgcn_readlane(rlo, bb);
+      p0 = __builtin_amdgcn_readlane(rp0, bb);
+      npg = __builtin_amdgcn_readlane(rnpg, bb);
+    } else {
+      decode_range(a, bb, L, lo, p0, npg);
+    }
+  };
 
   double rho_x[2] = {0.0, 0.0};  // exact K=V: frequencies of pairs 8(4c + j), c = 0, 1
   if constexpr (EXACT) {
@@ -301,7 +326,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(AttnArgs a) {
   int64_t u = u0;
   while (u < u1 && b < B) {
     int L, lo, p0, npg;
-    decode_range(a, b, L, lo, p0, npg);
+    seq_range(b, L, lo, p0, npg);
     const int64_t base = pref * Hkv;
     if (npg == 0 || u >= base + (int64_t)npg * Hkv) {
       pref += npg;
