@@ -46,6 +46,18 @@ def test_decode_matches_oracle(dtype, Hq, Hkv, D, W, cap, keqv, lens):
     assert_attn_close(out, ref, dtype, what=f"decode {dtype} D{D} G{Hq // Hkv} W{W} cap{cap}")
 
 
+@pytest.mark.parametrize("B", [64, 65, 130])
+@pytest.mark.parametrize("D,Hq,Hkv,W", [(256, 8, 4, 0), (512, 16, 2, 48)])
+def test_decode_batch_sizes_around_one_wave(B, D, Hq, Hkv, W):
+    """The decode set-up keeps the lengths of up to 64 sequences in the lanes of one wave and
+    loops over groups of 64 above that: batches at and past that boundary, ragged lengths."""
+    spec = wl.LayerSpec("bf16", Hq, Hkv, D, window=W, rope_theta=1e4 if D < 512 else 1e6)
+    g = np.random.default_rng(100 + B)
+    lens = [int(x) for x in g.integers(1, 120, size=B)]
+    out, ref = _decode_case(spec, lens, seed=23 + B)
+    assert_attn_close(out, ref, "bf16", what=f"decode B{B} D{D} W{W}")
+
+
 def test_decode_softcap_binds():
     """q scaled by 20 so that the cap of 50 dominates the scores."""
     spec = wl.LayerSpec("bf16", 8, 4, 256, softcap=50.0, scale=1 / 16, norm_q=False,
