@@ -8,7 +8,8 @@ prefill workload (4 x 2048 new tokens after 6144 cached, 5 sliding + 1 global la
 two other decode workloads, each with its own roofline fraction.
 
 value = algorithmic KV bytes read by decode attention per step / wall time per step (GB/s),
-with each step replayed from a HIP graph (as a serving loop would run it).  Inputs are
+with the timed steps replayed as one HIP graph of exactly that many consecutive steps (a
+serving loop replays one graph per iteration over all its layers).  Inputs are
 resident in HBM; the caches are rotated over several copies so that the 256 MB last-level
 cache cannot hold a step's working set.  The roofline figure times the attention call alone:
 back-to-back calls between two HIP events on the launch stream.
@@ -274,32 +275,37 @@ def prefill_global_kv_forms(pf: "PrefillBench", reps: int):
 
 # ----------------------------------------------------------------------------- timing ---------
 
-def capture_steps(step_fns):
-    """One HIP graph per step function (each runs the whole step: write + attention).  The
-    step is run eagerly first (warm-up, and the library's one-time device queries)."""
-    for f in step_fns:
-        f()
-    torch.cuda.synchronize()
-    graphs = []
-    for f in step_fns:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            f()
-        graphs.append(g)
-    torch.cuda.synchronize()
-    return graphs
+def capture_chain(step_fn, n):
+    """One HIP graph holding n consecutive steps step_fn(0) .. step_fn(n - 1).  A serving loop
+    replays one graph per decode iteration over all its layers, so a graph launch is paid once
+    per many layer steps; timing each step as its own graph would add a launch gap (about
+    8 us on the box) to every step."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            step_fn(i)
+    return g
 
 
-def time_graph_steps(graphs, steps, warmup):
-    """Wall-clock ms per step over `steps` graph replays (rotating over the graphs)."""
-    for i in range(warmup):
-        graphs[i % len(graphs)].replay()
+def time_chain(step_fn, n_distinct, steps, warmup):
+    """Wall-clock ms per step: the steps are run eagerly once per distinct input (warm-up, and
+    the library's one-time device queries), then `warmup` steps in one graph replay, then
+    exactly `steps` steps in one timed graph replay, synchronized on both sides."""
+    for i in range(n_distinct):
+        step_fn(i)
+    torch.cuda.synchronize()
+    gw = capture_chain(step_fn, warmup) if warmup > 0 else None
+    gt = capture_chain(step_fn, steps)
+    torch.cuda.synchronize()
+    if gw is not None:
+        gw.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        graphs[i % len(graphs)].replay()
+    gt.replay()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e3 / steps
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    del gw, gt
+    return ms
 
 
 def time_calls(fn, n, reps, warmup):
@@ -401,8 +407,7 @@ def main():
     # ---- headline: soft-capped decode -------------------------------------------------
     head = DecodeBench("softcap_decode_bf16", args.copies, dev)
     nc = len(head.kcs)
-    graphs = capture_steps([lambda c=c: (head.write(c), head.attend(c)) for c in range(nc)])
-    wall = time_graph_steps(graphs, args.steps, args.warmup)
+    wall = time_chain(lambda i: (head.write(i), head.attend(i)), nc, args.steps, args.warmup)
     a_ms = time_calls(head.attend, nc, args.steps, args.warmup)
     w_ms = time_calls(head.write, nc, args.steps, args.warmup)
     pct = call_percentiles(head.attend, nc, max(args.steps, 20), args.warmup)
@@ -410,7 +415,7 @@ def main():
     props = torch.cuda.get_device_properties(dev)
     value = head.bytes / (wall * 1e-3) / 1e9
     achieved = head.bytes / (a_ms * 1e-3) / 1e9
-    log(f"softcap_decode: step {wall * 1e3:.1f} us (graph replay); attention call "
+    log(f"softcap_decode: step {wall * 1e3:.1f} us ({args.steps} steps in one graph); attention call "
         f"{a_ms * 1e3:.1f} us -> {achieved:.0f} GB/s; write call {w_ms * 1e3:.1f} us; "
         f"{value:.0f} GB/s per step")
     result = {
@@ -429,7 +434,8 @@ def main():
         "config": {"workload": "softcap_decode_bf16", "batch": head.pb.batch,
                    "context_lens": "U[512,4096] seeded", "num_q_heads": 8, "num_kv_heads": 4,
                    "head_dim": 256, "softcap": 50.0, "scale": 0.0625, "block_size": BS,
-                   "step": "kv_cache_write(32 new tokens) + attn_decode, replayed as a HIP graph",
+                   "step": "kv_cache_write(32 new tokens) + attn_decode; the timed steps "
+                           "replayed as one HIP graph, each over the next cache copy",
                    "kv_bytes_per_step": head.bytes, "cache_copies_rotated": nc,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "attn_decode (decode_stream_kernel + "
@@ -444,7 +450,6 @@ def main():
                      "measured_copy_GBps": copy_gbs,
                      "device": {"name": props.name, "compute_units": props.multi_processor_count}},
     }
-    del graphs
     if not args.no_extra:
         extra = {}
         for name in ("sliding_decode_bf16", "kv_shared_decode_bf16",
@@ -454,8 +459,8 @@ def main():
             db = DecodeBench(base, 2 if base == "kv_shared_decode_bf16" else args.copies, dev,
                              exact=exact)
             n = len(db.kcs)
-            gx = capture_steps([lambda c=c: (db.write(c), db.attend(c)) for c in range(n)])
-            wall_x = time_graph_steps(gx, max(args.steps // 2, 5), max(args.warmup // 2, 2))
+            wall_x = time_chain(lambda i: (db.write(i), db.attend(i)), n,
+                                max(args.steps // 2, 5), max(args.warmup // 2, 2))
             a_x = time_calls(db.attend, n, max(args.steps // 2, 5), max(args.warmup // 2, 2))
             gbs = db.bytes / (a_x * 1e-3) / 1e9
             log(f"{name}: attention call {a_x * 1e3:.1f} us -> {gbs:.0f} GB/s "
@@ -464,17 +469,16 @@ def main():
                            "attn_GBps": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
                            "step_us": round(wall_x * 1e3, 2),
                            "step_GBps": round(db.bytes / (wall_x * 1e-3) / 1e9, 1)}
-            del gx, db
+            del db
             torch.cuda.empty_cache()
         pf = PrefillBench(dev)
         nl = len(pf.layers)
 
-        def stack():
+        def stack(i):
             for li in range(nl):
                 pf.write(li)
                 pf.attend(li)
-        gp = capture_steps([stack])
-        wall_p = time_graph_steps(gp, max(args.steps // 5, 3), max(args.warmup // 5, 1))
+        wall_p = time_chain(stack, 1, max(args.steps // 5, 3), max(args.warmup // 5, 1))
         a_layers = [time_calls(lambda i, li=li: pf.attend(li), 1, 3, 1) for li in range(nl)]
         w_layers = [time_calls(lambda i, li=li: pf.write(li), 1, 3, 1) for li in range(nl)]
         attn_ms = float(sum(a_layers))
@@ -496,7 +500,7 @@ def main():
             "separate_v": round(a_layers[-1], 4),
             **{f: round(ms, 4) for f, ms in forms.items()}}
         result["extra"] = extra
-        del gp, pf
+        del pf
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_decode(head, args.cpu_budget)

@@ -75,8 +75,6 @@ __device__ __forceinline__ uint32_t keep2(bool a, bool b) {
   return (a ? 0x0000ffffu : 0u) | (b ? 0xffff0000u : 0u);
 }
 
-// Row stride (elements) of a wave's LDS page buffer in the K=V path: 16 bytes of padding
-// shift consecutive rows by 4 banks so the column-wise reads of 4 rows hit distinct banks.
 // One page [16 keys][D] per wave for the K=V value reads, rows padded so that the rows of
 // a transposing read (4 keys x 4 columns per 16 lanes) fall 32 bytes apart in the banks.
 template <int D>
