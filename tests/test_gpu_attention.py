@@ -242,3 +242,83 @@ def test_decode_sequence_without_keys_gives_zero_output():
     ref = case.oracle_attention(qd, cu, cl)
     keep = [0, 2]
     assert_attn_close(out[keep], ref[keep], "bf16", what="decode with an empty sequence")
+
+
+def _stored_values(case, lens, G):
+    """The stored value of every position of every sequence, per query head, as the cache
+    holds it: [sum(lens)] rows of [Hq][D] (host bits or fp32), gathered through the table (the
+    V^T page is [d][row]; with K=V the stored keys, through the K layout)."""
+    kc, vc = case.host_caches()
+    unit = unit_elems(case.spec.dtype)
+    if vc is None:
+        kc = logical_k(kc, case.pb.block_table, lens, unit)  # [nb, Hkv, 16, D] as [row][d]
+    rows = []
+    for b, L in enumerate(lens):
+        for t in range(L):
+            blk = case.pb.block_table[b, t // wl.BLOCK_SIZE]
+            r = t % wl.BLOCK_SIZE
+            per_kv = vc[blk, :, :, r] if vc is not None else kc[blk, :, r, :]
+            rows.append(np.repeat(per_kv, G, axis=0))
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("dtype,keqv,cap", [("bf16", False, 0.0), ("bf16", True, 30.0),
+                                            ("fp32", False, 0.0), ("fp32", True, 0.0)])
+def test_window_of_one_returns_the_own_value_bit_exactly(dtype, keqv, cap):
+    """W = 1: every query sees only its own key, whose weight is exactly 1, so each output row
+    is the stored value of its own position, bit for bit (prefill rows and decode)."""
+    D, Hq, Hkv = 256, 8, 4
+    spec = wl.LayerSpec(dtype, Hq, Hkv, D, window=1, softcap=cap, k_eq_v=keqv, rope_theta=1e4,
+                        scale=1.0 if cap == 0 else 1.0 / 16)
+    lens, news = [40, 17, 70], [40, 9, 33]
+    pb = wl.paged_batch(lens, news, seed=61)
+    case = PagedCase(spec, pb, 61)
+    past = [L - n for L, n in zip(lens, news)]
+    case.write(past, past, 62, with_q=False)
+    _, _, _, qd, cu, cl = case.write(lens, news, 63)
+    out = wl.to_numpy_bits(case.prefill(qd, cu, cl))
+    dec = wl.to_numpy_bits(case.decode(qd[torch.from_numpy(cu[1:] - 1).long().to(qd.device)].contiguous(), cl))
+    torch.cuda.synchronize()
+    vals = _stored_values(case, lens, Hq // Hkv)
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    want_pre = np.concatenate([vals[starts[b] + past[b]:starts[b + 1]] for b in range(len(lens))])
+    want_dec = np.stack([vals[starts[b + 1] - 1] for b in range(len(lens))])
+    bits = (lambda x: x.view(np.uint32)) if dtype == "fp32" else (lambda x: x)
+    assert np.array_equal(bits(out), bits(want_pre))
+    assert np.array_equal(bits(dec), bits(want_dec))
+
+
+@pytest.mark.parametrize("D,Hq,Hkv", [(256, 8, 4), (512, 16, 2)])
+def test_window_beyond_every_length_equals_global(D, Hq, Hkv):
+    """W larger than every context sees exactly what a global layer sees: identical bits."""
+    outs = []
+    for W in (0, 1 << 20):
+        spec = wl.LayerSpec("bf16", Hq, Hkv, D, window=W, rope_theta=1e4)
+        lens, news = [300, 45, 129], [64, 45, 1]
+        pb = wl.paged_batch(lens, news, seed=71)
+        case = PagedCase(spec, pb, 71)
+        past = [L - n for L, n in zip(lens, news)]
+        case.write(past, past, 72, with_q=False)
+        _, _, _, qd, cu, cl = case.write(lens, news, 73)
+        pre = case.prefill(qd, cu, cl)
+        dec = case.decode(qd[torch.from_numpy(cu[1:] - 1).long().to(qd.device)].contiguous(), cl)
+        torch.cuda.synchronize()
+        outs.append((wl.to_numpy_bits(pre), wl.to_numpy_bits(dec)))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("D,W", [(256, 0), (512, 37)])
+def test_prefill_largest_group(D, W):
+    """16 query heads per kv head, the largest group the bf16 kernels take."""
+    spec = wl.LayerSpec("bf16", 16, 1, D, window=W, rope_theta=1e4 if D < 512 else 1e6)
+    lens, news = [150, 40], [70, 40]
+    pb = wl.paged_batch(lens, news, seed=81)
+    case = PagedCase(spec, pb, 81)
+    past = [L - n for L, n in zip(lens, news)]
+    case.write(past, past, 82, with_q=False)
+    _, _, _, qd, cu, cl = case.write(lens, news, 83)
+    out = case.prefill(qd, cu, cl)
+    torch.cuda.synchronize()
+    ref = case.oracle_attention(qd, cu, cl)
+    assert_attn_close(out, ref, "bf16", what=f"prefill G16 D{D} W{W}")
