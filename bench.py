@@ -415,9 +415,9 @@ def main():
     props = torch.cuda.get_device_properties(dev)
     value = head.bytes / (wall * 1e-3) / 1e9
     achieved = head.bytes / (a_ms * 1e-3) / 1e9
-    log(f"softcap_decode: step {wall * 1e3:.1f} us ({args.steps} steps in one graph); attention call "
-        f"{a_ms * 1e3:.1f} us -> {achieved:.0f} GB/s; write call {w_ms * 1e3:.1f} us; "
-        f"{value:.0f} GB/s per step")
+    log(f"softcap_decode: step {wall * 1e3:.1f} us ({args.steps} steps in one graph); "
+        f"attention call {a_ms * 1e3:.1f} us -> {achieved:.0f} GB/s; "
+        f"write call {w_ms * 1e3:.1f} us; {value:.0f} GB/s per step")
     result = {
         "metric": "decode attn KV GB/s (% HBM peak); prefill attn TFLOP/s (% MFMA peak)",
         "value": round(value, 2),

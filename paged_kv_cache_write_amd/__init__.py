@@ -240,4 +240,5 @@ def check_metadata_host(p: LayerParams, cu_seqlens, context_lens, block_table, n
 __all__ = ["LayerParams", "layer_params", "kv_cache_write", "attn_decode", "attn_prefill",
            "decode_workspace_bytes", "decode_workspace", "check_metadata_host", "GAError",
            "load_library", "LIB_PATH", "DEBUG_LIB_PATH", "select_library", "debug_take_error",
-           "DEBUG_BLOCK_ID", "DEBUG_LENGTH", "DEBUG_BOUND", "DEBUG_OWNER", "GA_FP32", "GA_BF16", "BLOCK_SIZE"]
+           "DEBUG_BLOCK_ID", "DEBUG_LENGTH", "DEBUG_BOUND", "DEBUG_OWNER", "GA_FP32", "GA_BF16",
+           "BLOCK_SIZE"]

@@ -5,12 +5,13 @@
 // last min(len, W) keys; head-first GQA).  [KUNLUN] = "Gemma 4 模型架构解析" §6.5 (attention
 // reads K/V through the block table).  [MNN] = "MNN 支持 Gemma4 全系列" §6.2 (K=V).
 //
-// Load balance.  The visible pages of all (sequence, kv head) segments are laid end to end and
-// cut into `nworkers` equal runs, one per single-wave worker (as many as the device holds at
-// once for this kernel, so the whole grid is resident in one round).  Ragged lengths therefore cost nothing: every worker streams the
-// same number of pages.  A worker whose run crosses segment boundaries emits one partial
-// (m, l, o) per segment piece; piece (worker w, segment s) is stored at index w + s, which is
-// unique, and the pieces of one segment are consecutive, so the merge reads a contiguous range.
+// Load balance.  The visible pages of all (sequence, kv head) segments are laid end to end and cut
+// into `nworkers` equal runs, one per single-wave worker (as many as the device holds at once for
+// this kernel, so the whole grid is resident in one round).  Ragged lengths therefore cost nothing:
+// every worker streams the same number of pages.  A worker whose run crosses segment boundaries
+// emits one partial (m, l, o) per segment piece; piece (worker w, segment s) is stored at
+// index w + s, which is unique, and the pieces of one segment are consecutive, so the merge
+// reads a contiguous range.
 //
 // Pipelining.  A worker keeps one step (two pages; one at head size 512 or with K=V) of K and V
 // in registers: the next step's K loads are issued as soon as the current step's QK^T products
@@ -214,7 +215,8 @@ __device__ __forceinline__ void decode_piece(const AttnArgs& a, const bf16x8_t (
           acc.o[n] = mfma_16x16x32(as_bf16x8(u32x4_t{va.x, va.y, vb.x, vb.y}), pf, acc.o[n]);
         }
       } else {
-        const short4_t pf = as_short4(u32x2_t{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])});
+        const short4_t pf =
+            as_short4(u32x2_t{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])});
         const uint32_t m01 = keep2(vk[0], vk[1]), m23 = keep2(vk[2], vk[3]);
 #pragma unroll
         for (int n = 0; n < ND; ++n) {
@@ -437,7 +439,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
     if (i < ns) acc += wts[i] * pre[k];
   }
 #pragma unroll 4
-  for (int i = gi + kPre * NG; i < ns; i += NG) acc += wts[i] * *(const float4_t*)(ocol + i * ostep);
+  for (int i = gi + kPre * NG; i < ns; i += NG)
+    acc += wts[i] * *(const float4_t*)(ocol + i * ostep);
   part[t] = acc;
   __syncthreads();
   if (gi == 0) {

@@ -7,12 +7,13 @@
 // frequencies, in double precision -- once into LDS, and each of its 4 wavefronts takes one
 // (token, head) row at a time.  Large batches give a workgroup all slots of its token;
 // small ones (a decode step) split a token's slots over several workgroups so that the launch
-// still fills the chip.  Each wave issues the loads of 4 rows before it processes the first.  With rotate-half RoPE the
-// pair (k, k + D/2) must sit in one lane, so lane l holds the C = D/128 consecutive elements
-// starting at l*C of the first half and the matching C of the second half.  The norm's sum of
-// squares is a wavefront reduction; the norm and the rotation run in double precision and the
-// result is rounded once into the storage type (bf16: round-to-odd to fp32, then to nearest
-// even), so the stored cache does not depend on the order of the arithmetic.
+// still fills the chip.  Each wave issues the loads of 4 rows before it processes the first.
+// With rotate-half RoPE the pair (k, k + D/2) must sit in one lane, so lane l holds the
+// C = D/128 consecutive elements starting at l*C of the first half and the matching C of the
+// second half.  The norm's sum of squares is a wavefront reduction; the norm and the rotation
+// run in double precision and the result is rounded once into the storage type (bf16:
+// round-to-odd to fp32, then to nearest even), so the stored cache does not depend on the
+// order of the arithmetic.
 //
 // Sources: [KUNLUN] = "Gemma 4 模型架构解析" (vLLM-Kunlun adaptation guide), §4.3 (a layer that
 // owns its cache norms k, rotates q and k, norms v), §6.3 (slot = page id * 16 + row), §6.4
