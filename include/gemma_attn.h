@@ -31,7 +31,8 @@
  *     device memory (lengths, block ids) cannot be read by the host without a copy: validate
  *     them with ga_check_metadata_host on host copies.  The kernels clamp every page index and
  *     block id into the buffers they were given, so bad metadata yields wrong numbers but no
- *     out-of-bounds access.
+ *     out-of-bounds access.  The debug build (libgemma_attn_debug.so) also checks that metadata
+ *     in the kernels and reports it through ga_debug_take_error (at the end of this header).
  *   - ga_last_error() returns a thread-local, human-readable reason for the last failure.
  *
  * Paged cache layout (block_size 16, the default page size of vLLM's paged cache; [KUNLUN] §6.3
