@@ -23,7 +23,9 @@
  * Conventions for every call
  *   - Pointers marked DEVICE are device (HBM) addresses; HOST ones are host addresses.  All
  *     buffers are owned by the caller; the library allocates nothing, frees nothing and keeps
- *     no state between calls, so it is safe to call from several host threads.
+ *     no state between calls, so it is safe to call from several host threads.  The one
+ *     exception is ga_attn_decode_noalloc, whose scratch is a fixed device array of the
+ *     library (one per device) that its calls share.
  *   - `stream` is a hipStream_t (NULL: the default stream).  Every call only enqueues work on
  *     it and returns; nothing is synchronised.
  *   - Scalar arguments and the params struct are checked on the host before anything is
@@ -180,6 +182,25 @@ ga_status ga_attn_decode(const ga_layer_params* p, const void* q, const void* k_
                          int32_t max_blocks, const int32_t* context_lens, int32_t batch,
                          int32_t max_context_len, void* out, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/* Decode attention without a caller-supplied workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, results and errors as ga_attn_decode, minus `workspace` and
+ * `workspace_bytes`: the scratch lives in a fixed array of GA_DECODE_NOALLOC_SCRATCH_BYTES in
+ * device memory that the library holds on every device it runs on until the process ends.
+ * A shape whose ga_decode_workspace_bytes exceeds that size is refused with GA_ERR_WORKSPACE
+ * before anything touches the device.  The call allocates nothing: the array's device address
+ * is looked up once per device, on the first call with that device current.  Every call on one
+ * device shares the array, so calls that may overlap on one device (several streams, several
+ * host threads) race and give wrong results: serialise them, or use ga_attn_decode with a
+ * workspace each.  The decode kernels overwrite the scratch before reading it, so nothing left
+ * by an earlier call leaks into a later one. */
+#define GA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
+ga_status ga_attn_decode_noalloc(const ga_layer_params* p, const void* q, const void* k_cache,
+                                 const void* v_cache, int64_t num_blocks,
+                                 const int32_t* block_table, int32_t max_blocks,
+                                 const int32_t* context_lens, int32_t batch,
+                                 int32_t max_context_len, void* out, void* stream);
 
 /* Prefill / chunked prefill: the n_b new queries of each sequence, packed, against its cache
  * (the chunk's own keys must already be written).  Query i of sequence b sits at position

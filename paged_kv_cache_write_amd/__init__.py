@@ -89,6 +89,8 @@ def load_library():
     lib.ga_decode_workspace_bytes.argtypes = [PP, i32, i32]
     lib.ga_attn_decode.restype = ctypes.c_int
     lib.ga_attn_decode.argtypes = [PP, P, P, P, i64, P, i32, P, i32, i32, P, P, sz, P]
+    lib.ga_attn_decode_noalloc.restype = ctypes.c_int
+    lib.ga_attn_decode_noalloc.argtypes = [PP, P, P, P, i64, P, i32, P, i32, i32, P, P]
     lib.ga_attn_prefill.restype = ctypes.c_int
     lib.ga_attn_prefill.argtypes = [PP, P, P, P, P, i64, P, i32, P, i32, i32, i32, P, P]
     lib.ga_check_metadata_host.restype = ctypes.c_int
@@ -206,6 +208,28 @@ def attn_decode(p: LayerParams, q, k_cache, v_cache, block_table, context_lens,
     return out
 
 
+# GA_DECODE_NOALLOC_SCRATCH_BYTES of the header: the largest decode workspace that
+# attn_decode_noalloc serves from the library's own device array
+DECODE_NOALLOC_SCRATCH_BYTES = 48 << 20
+
+
+def attn_decode_noalloc(p: LayerParams, q, k_cache, v_cache, block_table, context_lens,
+                        max_context_len: int, out, stream=None):
+    """ga_attn_decode_noalloc: decode into the caller's `out` [B, Hq, D] with the library's own
+    scratch (no allocation by the library or by this binding).  Calls on one device share that
+    scratch: calls that may overlap on one device race."""
+    lib = load_library()
+    et = _elem(p)
+    st = lib.ga_attn_decode_noalloc(
+        ctypes.byref(p), _ptr(q, "q", et), _ptr(k_cache, "k_cache", et),
+        _ptr(v_cache, "v_cache", et), k_cache.shape[0],
+        _ptr(block_table, "block_table", torch.int32), block_table.shape[1],
+        _ptr(context_lens, "context_lens", torch.int32), context_lens.shape[0],
+        int(max_context_len), _ptr(out, "out", et), _stream(stream))
+    _raise_on(st)
+    return out
+
+
 def attn_prefill(p: LayerParams, q, cu_seqlens_q, k_cache, v_cache, block_table, context_lens,
                  max_q_len: int, out=None, stream=None):
     """ga_attn_prefill: returns out [total_q, Hq, D]."""
@@ -238,6 +262,7 @@ def check_metadata_host(p: LayerParams, cu_seqlens, context_lens, block_table, n
 
 
 __all__ = ["LayerParams", "layer_params", "kv_cache_write", "attn_decode", "attn_prefill",
+           "attn_decode_noalloc", "DECODE_NOALLOC_SCRATCH_BYTES",
            "decode_workspace_bytes", "decode_workspace", "check_metadata_host", "GAError",
            "load_library", "LIB_PATH", "DEBUG_LIB_PATH", "select_library", "debug_take_error",
            "DEBUG_BLOCK_ID", "DEBUG_LENGTH", "DEBUG_BOUND", "DEBUG_OWNER", "GA_FP32", "GA_BF16",

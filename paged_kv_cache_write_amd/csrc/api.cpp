@@ -228,11 +228,12 @@ size_t ga_decode_workspace_bytes(const ga_layer_params* p, int32_t batch,
       .workspace_bytes;
 }
 
-ga_status ga_attn_decode(const ga_layer_params* p, const void* q, const void* k_cache,
-                         const void* v_cache, int64_t num_blocks, const int32_t* block_table,
-                         int32_t max_blocks, const int32_t* context_lens, int32_t batch,
-                         int32_t max_context_len, void* out, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+// Checks shared by both decode entry points; on success *plan holds the launch plan.
+static ga_status check_decode(const ga_layer_params* p, const void* q, const void* k_cache,
+                              const void* v_cache, int64_t num_blocks,
+                              const int32_t* block_table, int32_t max_blocks,
+                              const int32_t* context_lens, int32_t batch,
+                              int32_t max_context_len, const void* out, ga::DecodePlan* plan) {
   ga_status s = check_attn_params(p);
   if (s != GA_OK) return s;
   if ((s = check_table(max_blocks, num_blocks, batch)) != GA_OK) return s;
@@ -258,19 +259,18 @@ ga_status ga_attn_decode(const ga_layer_params* p, const void* q, const void* k_
     if ((int64_t)batch * pages > 0x7fffffffLL)
       return fail(GA_ERR_UNSUPPORTED, "batch x visible pages per sequence exceeds 2^31");
   }
-  const ga::DecodePlan plan = ga::plan_decode(p->head_dim, p->num_q_heads, p->num_kv_heads,
-                                              p->window, batch, max_context_len,
-                                              p->dtype == GA_BF16);
-  if (plan.workspace_bytes > 0) {
-    if (!workspace) return fail(GA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)",
-                                plan.workspace_bytes);
-    if (workspace_bytes < plan.workspace_bytes)
-      return fail(GA_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes,
-                  plan.workspace_bytes);
-    if (((uintptr_t)workspace & 255) != 0)
-      return fail(GA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
-  }
-  if (batch == 0) return ok();
+  *plan = ga::plan_decode(p->head_dim, p->num_q_heads, p->num_kv_heads, p->window, batch,
+                          max_context_len, p->dtype == GA_BF16);
+  return GA_OK;
+}
+
+static ga_status launch_decode_checked(const ga_layer_params* p, const void* q,
+                                       const void* k_cache, const void* v_cache,
+                                       int64_t num_blocks, const int32_t* block_table,
+                                       int32_t max_blocks, const int32_t* context_lens,
+                                       int32_t batch, int32_t max_context_len, void* out,
+                                       void* workspace, const ga::DecodePlan& plan,
+                                       void* stream) {
   ga::AttnLaunch a = make_attn(p);
   a.q = q;
   a.k_cache = k_cache;
@@ -284,6 +284,56 @@ ga_status ga_attn_decode(const ga_layer_params* p, const void* q, const void* k_
   a.out = out;
   a.workspace = workspace;
   return from_hip(ga::launch_decode(a, plan, (hipStream_t)stream), "attn_decode launch");
+}
+
+ga_status ga_attn_decode(const ga_layer_params* p, const void* q, const void* k_cache,
+                         const void* v_cache, int64_t num_blocks, const int32_t* block_table,
+                         int32_t max_blocks, const int32_t* context_lens, int32_t batch,
+                         int32_t max_context_len, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  ga::DecodePlan plan;
+  ga_status s = check_decode(p, q, k_cache, v_cache, num_blocks, block_table, max_blocks,
+                             context_lens, batch, max_context_len, out, &plan);
+  if (s != GA_OK) return s;
+  if (plan.workspace_bytes > 0) {
+    if (!workspace) return fail(GA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)",
+                                plan.workspace_bytes);
+    if (workspace_bytes < plan.workspace_bytes)
+      return fail(GA_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes,
+                  plan.workspace_bytes);
+    if (((uintptr_t)workspace & 255) != 0)
+      return fail(GA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  }
+  if (batch == 0) return ok();
+  return launch_decode_checked(p, q, k_cache, v_cache, num_blocks, block_table, max_blocks,
+                               context_lens, batch, max_context_len, out, workspace, plan,
+                               stream);
+}
+
+ga_status ga_attn_decode_noalloc(const ga_layer_params* p, const void* q, const void* k_cache,
+                                 const void* v_cache, int64_t num_blocks,
+                                 const int32_t* block_table, int32_t max_blocks,
+                                 const int32_t* context_lens, int32_t batch,
+                                 int32_t max_context_len, void* out, void* stream) {
+  static_assert(GA_DECODE_NOALLOC_SCRATCH_BYTES == ga::kNoAllocScratchBytes,
+                "scratch size of the header and of the decode kernels");
+  ga::DecodePlan plan;
+  ga_status s = check_decode(p, q, k_cache, v_cache, num_blocks, block_table, max_blocks,
+                             context_lens, batch, max_context_len, out, &plan);
+  if (s != GA_OK) return s;
+  // the size is checked before the device is touched
+  if (plan.workspace_bytes > ga::kNoAllocScratchBytes)
+    return fail(GA_ERR_WORKSPACE, "this shape needs %zu bytes of decode scratch; the "
+                "allocation-free entry point holds at most %zu (use ga_attn_decode with a "
+                "workspace)", plan.workspace_bytes, (size_t)ga::kNoAllocScratchBytes);
+  if (batch == 0) return ok();
+  void* scratch = nullptr;
+  if (plan.workspace_bytes > 0) {
+    const hipError_t e = ga::decode_scratch_address(&scratch);
+    if (e != hipSuccess) return from_hip(e, "decode scratch address");
+  }
+  return launch_decode_checked(p, q, k_cache, v_cache, num_blocks, block_table, max_blocks,
+                               context_lens, batch, max_context_len, out, scratch, plan, stream);
 }
 
 ga_status ga_attn_prefill(const ga_layer_params* p, const void* q,

@@ -19,6 +19,7 @@
 // flight while the softmax and matrix-core work of the current step run.  The block ids of a
 // piece are fetched 64 at a time into one lane-register each and read back with readlane.
 #include <atomic>
+#include <mutex>
 
 #include "attn_common.hpp"
 
@@ -514,6 +515,32 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 
 GA_DEBUG_TAKE_DEFINE(debug_take_decode)
+
+// Scratch of ga_attn_decode_noalloc: a fixed-size array in device memory, one per device, held
+// until the process ends.  In host code `scratch` names a host-side stand-in, not the device
+// array, so kernels and copies only ever get the address hipGetSymbolAddress returns for the
+// current device.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t decode_scratch_address(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 DecodePlan plan_decode(int D, int Hq, int Hkv, int window, int batch, int max_context_len,
                        bool bf16) {

@@ -66,6 +66,12 @@ struct DecodePlan {
 DecodePlan plan_decode(int D, int Hq, int Hkv, int window, int batch, int max_context_len,
                        bool bf16);
 
+// Decode scratch of the allocation-free entry point: a file-scope device array of decode.hip,
+// one copy per device, shared by every call on that device.
+constexpr size_t kNoAllocScratchBytes = size_t(48) << 20;
+// Device address of that array on the current device (looked up once per device).
+hipError_t decode_scratch_address(void** ptr);
+
 hipError_t launch_kv_write(const KvWriteLaunch& a, hipStream_t s);
 hipError_t launch_decode(const AttnLaunch& a, const DecodePlan& plan, hipStream_t s);
 hipError_t launch_prefill(const AttnLaunch& a, hipStream_t s);

@@ -273,3 +273,44 @@ def test_binding_refuses_host_tensors():
                        torch.zeros(2, 4, dtype=torch.int32), cl, 64,
                        out=torch.zeros(2, 8, 256, dtype=torch.bfloat16),
                        workspace=torch.zeros(1 << 20, dtype=torch.uint8))
+
+
+def call_decode_noalloc(p, **kw):
+    lib = ga.load_library()
+    a = dict(q=FAKE, k_cache=FAKE, v_cache=None if p.k_eq_v else FAKE, num_blocks=10,
+             block_table=FAKE, max_blocks=4, context_lens=FAKE, batch=2, max_context_len=64,
+             out=FAKE, stream=None)
+    a.update(kw)
+    st = lib.ga_attn_decode_noalloc(ctypes.byref(p), a["q"], a["k_cache"], a["v_cache"],
+                                    a["num_blocks"], a["block_table"], a["max_blocks"],
+                                    a["context_lens"], a["batch"], a["max_context_len"],
+                                    a["out"], a["stream"])
+    return st, lib.ga_last_error().decode()
+
+
+def test_decode_noalloc_refuses_shapes_beyond_its_scratch():
+    """The allocation-free decode refuses a shape whose workspace exceeds the library's array,
+    on the host and before the device is touched (no GPU here)."""
+    p = good(num_q_heads=32, num_kv_heads=2, head_dim=512, rope_theta=1e6)
+    need = ga.decode_workspace_bytes(p, 64, 60000)
+    assert need > ga.DECODE_NOALLOC_SCRATCH_BYTES
+    st, msg = call_decode_noalloc(p, batch=64, max_blocks=3750, max_context_len=60000)
+    assert st == WORKSPACE and "allocation-free" in msg and str(need) in msg
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(q=None), INVALID, "required"),
+    (dict(max_context_len=0), INVALID, "max_context_len"),
+    (dict(max_context_len=65), INVALID, "max_blocks"),
+])
+def test_decode_noalloc_validates_like_decode(kw, code, msg):
+    st, err = call_decode_noalloc(good(), **kw)
+    assert st == code and msg in err
+    st2, err2 = call_decode(good(), **kw)
+    assert st2 == code and err2 == err
+
+
+def test_decode_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define GA_DECODE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == ga.DECODE_NOALLOC_SCRATCH_BYTES
