@@ -6,8 +6,14 @@ path.  The arithmetic lives in ``ga_ref.c`` (double precision, plain loops); thi
 that file with gcc and wraps it with ctypes over numpy arrays.
 
 bf16 tensors cross this boundary as ``numpy.uint16`` bit patterns, fp32 as ``numpy.float32``.
-Cache layouts are the library's documented ones: K pages ``[blk][g][off][d]``, V pages
-``[blk][g][d][off]``.
+Cache layouts are the library's documented ones (array shapes ``[blk][g][16][D]`` for K and
+``[blk][g][D][16]`` for V):
+
+* a K page ``[blk][g]`` holds its 16 key rows in 16-byte units: unit (row r, x) holds elements
+  x*U .. x*U+U-1 of row r (U = 8 for bf16, 4 for fp32) at unit slot
+  16*x + (r + 4*(lp % 2) + 4*((x // 8) % 2)) % 16, lp being the page's logical index
+  (position // 16) in its sequence;
+* a V page ``[blk][g]`` is transposed: element d of the key in row r sits at ``[d][r]``.
 """
 from __future__ import annotations
 

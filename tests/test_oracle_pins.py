@@ -275,6 +275,33 @@ def test_rope_equals_complex_rotation_of_half_pairs():
                                atol=1e-11)
 
 
+@pytest.mark.parametrize("D,theta,n,f", [(512, 1e6, 64, 1.0), (256, 1e4, 0, 1.0),
+                                         (128, 1e4, 0, 8.0), (8, 10.0, 1, 1.0)])
+def test_rope_rows_rotates_each_row_at_its_own_position(D, theta, n, f):
+    """The batched rotation (every row x[i] at its own position t[i]) against the complex form
+    z_k * exp(i (t_i / f) w_k), w_k = theta^(-2k/D) for k < n (all pairs when n = 0) and 0
+    above, built here from the page's frequency list; and row by row equal to the single-vector
+    rotation.  Positions are mixed (0, small, large, repeated, descending) so a wrong row or
+    position stride fails."""
+    rng = np.random.default_rng(D + n)
+    t = np.array([0.0, 1.0, 36043.0, 5.0, 5.0, 4099.0, 2.0, 17.0, 1000.0, 31337.0])
+    x = rng.standard_normal((len(t), D))
+    nr = n if n else D // 2
+    w = np.concatenate([1.0 / theta ** (np.arange(0, 2 * nr, 2, dtype=np.float64) / D),
+                        np.zeros(D // 2 - nr)])
+    y = oracle.rope_rows(x, t, theta, n, f)
+    for i in range(len(t)):
+        zc = (x[i, :D // 2] + 1j * x[i, D // 2:]) * np.exp(1j * (t[i] / f) * w)
+        np.testing.assert_allclose(y[i], np.concatenate([zc.real, zc.imag]), rtol=0,
+                                   atol=1e-11 * max(1.0, t[i] / f * w.max()))
+        np.testing.assert_array_equal(y[i], oracle.rope(x[i], t[i], theta, n, f))
+    # rows travel with their positions
+    perm = rng.permutation(len(t))
+    np.testing.assert_array_equal(oracle.rope_rows(x[perm], t[perm], theta, n, f), y[perm])
+    # the input is not modified and a single row works
+    np.testing.assert_array_equal(oracle.rope_rows(x[3:4], t[3:4], theta, n, f), y[3:4])
+
+
 def _pair_angles(D, theta, angles=0, pos_scale=1.0, t=1.0):
     """Angle each pair (k, k + D/2) turns by, read back by rotating the unit vectors e_k."""
     out = np.empty(D // 2)
