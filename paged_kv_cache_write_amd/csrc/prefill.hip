@@ -49,9 +49,10 @@
 // The tile loop issues no vector-memory operation other than the tile copies (the Q loads
 // are complete before it starts), so the copies' completion is counted exactly.
 //
-// Order of work: workgroup ids are dealt to the 8 XCDs round robin, so consecutive logical
-// tiles are given to one XCD (its L2 then serves the key tiles shared by neighbouring row
-// tiles), and within a (sequence, kv head) the row tiles with the most keys start first.
+// Order of work: workgroup ids are dealt to the 8 XCDs round robin.  Runs of kRun neighbouring
+// row tiles of one (sequence, kv head) go to one XCD (its L2 then serves the key tiles they
+// share), the runs of every (sequence, kv head) are spread over all 8 XCDs (so chunks of
+// different lengths load the XCDs evenly), and the row tiles with the most keys start first.
 #include "prefill_common.hpp"
 
 namespace ga {
@@ -59,6 +60,7 @@ namespace {
 
 constexpr int kWaves = 8;             // two waves per SIMD, 256 registers each
 constexpr int kPF = 3;                // operand fragment reads in flight ahead of their products
+constexpr int kRun = 4;               // consecutive row tiles of a group given to one XCD
 
 // MFMA column blocks per wave: 2 (32 rows) up to head size 256, 1 (16 rows) at 512, where
 // 32 rows of Q^T (128 registers) plus O^T (256) would not fit a wave's 256 registers.
@@ -167,8 +169,8 @@ constexpr int rope_chunk_of() {
 // pair per thread) into a separate LDS buffer that the QK^T fragment reads of those chunks
 // use; the values are still read from the unrotated tile.
 template <int D, int SM, bool KEQV, bool EXACT>
-__global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs a, int tiles_per_bg,
-                                                                     int n_tiles) {
+__global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs a, int runs_per_bg,
+                                                                     int n_groups) {
   using T = TileLds<D, KEQV>;
   constexpr int NC = D / 32, ND = D / 16, R = Rows<D>::kR, SK = T::SK, SV = T::SV;
   constexpr int kRowsPerWave = Rows<D>::kPerWave, kRowsPerWg = Rows<D>::kPerWg;
@@ -178,13 +180,18 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
   const int lane = threadIdx.x & 63, c16 = lane & 15, j = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  // ---- which (sequence, kv head, row tile) this workgroup owns (XCD-contiguous order):
-  // the grid is a multiple of 8, so this is a bijection of [0, gridDim.x); the padding returns
-  const int per_xcd = gridDim.x / 8;
-  const int logical = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (logical >= n_tiles) return;
-  const int bg = logical / tiles_per_bg;
-  const int rt = tiles_per_bg - 1 - (logical - bg * tiles_per_bg);  // most keys first
+  // ---- which (sequence, kv head, row tile) this workgroup owns.  Work items are (group bg,
+  // rank r), r = 0 being the group's row tile with the most keys (its last one).  Each group's
+  // ranks are cut into runs of kRun consecutive ranks and the runs, group-major, are dealt to
+  // the 8 XCDs round robin (workgroup i runs on XCD i mod 8): every XCD gets about an eighth of
+  // every group whatever the chunk lengths, while the row tiles running together on one XCD
+  // are neighbours that share most of their key tiles in its L2.  Ranks past a group's own
+  // row tiles (a shorter chunk than max_q_len) and the padding of the grid return at once.
+  const int xcd = blockIdx.x % 8, kq = blockIdx.x / 8;
+  const int run = 8 * (kq / kRun) + xcd;
+  const int bg = run / runs_per_bg;
+  const int rank = (run - bg * runs_per_bg) * kRun + kq % kRun;
+  if (bg >= n_groups) return;
   const int b = bg / a.Hkv, g = bg - (bg / a.Hkv) * a.Hkv;
   if (b >= a.batch) return;
   const int G = a.G, W = a.window;
@@ -198,8 +205,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
   L = L > a.max_ctx ? a.max_ctx : L;
   const int past = L - n;
   if (past < 0) debug_flag(kDbgLength);
-  const int row0 = rt * kRowsPerWg;
-  if (q0 < 0 || n <= 0 || past < 0 || row0 >= n * G) return;  // uniform over the workgroup
+  const int tiles_b = (n * G + kRowsPerWg - 1) / kRowsPerWg;  // row tiles of this group
+  if (q0 < 0 || n <= 0 || past < 0 || rank >= tiles_b) return;  // uniform over the workgroup
+  const int row0 = (tiles_b - 1 - rank) * kRowsPerWg;
 
   // ---- key tiles of the workgroup: keys [lo(first row), position(last row)]
   const int nrows_wg = (n * G - row0) < kRowsPerWg ? (n * G - row0) : kRowsPerWg;
@@ -584,17 +592,21 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   using T = TileLds<D, KEQV>;
   constexpr int kLds = T::kBytes + (EXACT ? T::kRopeBytes : 0);
   constexpr int kRowsPerWg = Rows<D>::kPerWg;
-  const int tiles_per_bg = (a.max_q_len * a.G + kRowsPerWg - 1) / kRowsPerWg;
-  const int n_tiles = tiles_per_bg * a.Hkv * a.batch;
-  if (n_tiles == 0) return hipSuccess;
-  const int grid = (n_tiles + 7) / 8 * 8;  // whole rounds over the 8 XCDs
+  const int64_t tiles_per_bg = ((int64_t)a.max_q_len * a.G + kRowsPerWg - 1) / kRowsPerWg;
+  const int64_t runs_per_bg = (tiles_per_bg + kRun - 1) / kRun;
+  const int64_t n_groups = (int64_t)a.Hkv * a.batch;
+  const int64_t runs = runs_per_bg * n_groups;
+  if (runs == 0) return hipSuccess;
+  const int64_t grid = (runs + 7) / 8 * 8 * kRun;  // whole rounds of runs over the 8 XCDs
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
   static_assert(kLds <= 160 * 1024, "LDS budget");
   hipError_t e = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&prefill_tiled_kernel<D, SM, KEQV, EXACT>),
       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((prefill_tiled_kernel<D, SM, KEQV, EXACT>), dim3(grid), dim3(64 * kWaves),
-                     kLds, s, a, tiles_per_bg, n_tiles);
+  hipLaunchKernelGGL((prefill_tiled_kernel<D, SM, KEQV, EXACT>), dim3((unsigned)grid),
+                     dim3(64 * kWaves),
+                     kLds, s, a, (int)runs_per_bg, (int)n_groups);
   return hipGetLastError();
 }
 

@@ -167,6 +167,19 @@ def jittered_lengths(B: int, lo: int, hi: int, seed: int) -> np.ndarray:
     return torch.randint(lo, hi + 1, (B,), generator=g).numpy().astype(np.int32)
 
 
+def chunk_lengths(seed: int, B: int = 4, n_mean: int = 2048, n_jit: int = 256,
+                  past_lo: int = 5632, past_hi: int = 6656):
+    """Seeded varlen chunk shapes: new tokens n_b = n_mean + U_int[-n_jit, n_jit] with the
+    last one adjusted so that sum(n_b) = B * n_mean exactly, and past_b ~ U_int[past_lo,
+    past_hi].  Returns (n, past) as int32 arrays."""
+    g = torch.Generator().manual_seed(3000 + seed)
+    d = torch.randint(-n_jit, n_jit + 1, (B,), generator=g).numpy().astype(np.int64)
+    d[-1] = -d[:-1].sum()
+    n = (n_mean + d).astype(np.int32)
+    past = torch.randint(past_lo, past_hi + 1, (B,), generator=g).numpy().astype(np.int32)
+    return n, past
+
+
 def workload(name: str):
     """(LayerSpec list, PagedBatch) of a named workload.
 
@@ -174,8 +187,10 @@ def workload(name: str):
     softcap_decode_bf16  32 seqs, L ~ U[512, 4096], 8/4 heads, D 256, cap 50, scale 1/16
     sliding_decode_bf16  64 seqs, L 8192, W 1024, 32/16 heads, D 256, norms, theta 1e4
     kv_shared_decode_bf16 16 seqs, L ~ U[29491, 36044], 32/4 heads, D 512, K=V, theta 1e6
-    chunked_prefill_bf16 4 seqs, 2048 new after 6144 past; 5 sliding layers (W 1024, D 256,
-                         32/16 heads) + 1 global layer (D 512, 32/4 heads, theta 1e6)
+    chunked_prefill_bf16 4 seqs, varlen chunks: n_b = 2048 +- up to 256 (8192 new tokens in
+                         all) appended after past_b ~ U[5632, 6656] cached tokens (seeded);
+                         5 sliding layers (W 1024, D 256, 32/16 heads) + 1 global layer (D 512,
+                         32/4 heads, theta 1e6)
     """
     if name == "tiny_sliding_fp32":
         # the table covers the final 272 tokens (17 pages) plus 15 spare: 32 blocks in all
@@ -196,7 +211,8 @@ def workload(name: str):
     if name == "chunked_prefill_bf16":
         sliding = LayerSpec("bf16", 32, 16, 256, window=1024, rope_theta=1e4)
         glob = LayerSpec("bf16", 32, 4, 512, window=0, rope_theta=1e6)
-        pb = paged_batch(np.full(4, 8192), np.full(4, 2048), seed=5)
+        news, past = chunk_lengths(seed=5)
+        pb = paged_batch(past + news, news, seed=5)
         return [sliding] * 5 + [glob], pb
     raise KeyError(name)
 
