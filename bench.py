@@ -1,18 +1,21 @@
 """Benchmark of the paged-KV Gemma attention hot path on one MI355X.
 
-A step is one pass of the path over one batch: ga_kv_cache_write of the batch's new tokens
-(norm + RoPE + scatter), then the attention call over the paged cache.  The headline line
-measures the bf16 soft-capped decode workload (32 sequences, lengths U[512, 4096], 8 query /
-4 kv heads, head size 256, cap 50, scale 1/16); the same JSON line also carries the chunked
-prefill workload (4 x 2048 new tokens after 6144 cached, 5 sliding + 1 global layer) and the
-two other decode workloads, each with its own roofline fraction.
+A step is one pass of the whole path over one batch: ga_kv_cache_write of the batch's new
+tokens (norm + RoPE + scatter), then the attention call over the paged cache.  The headline line
+measures the largest single-GPU workload, the global-layer K=V decode (16 sequences of about 32k
+tokens, 32 query / 4 kv heads, head size 512, keys reused as values, about 2.1 GB of K per
+call); the same JSON line carries every other workload (the soft-capped decode, the sliding
+decode, the chunked-prefill stack of 5 sliding + 1 global layer, the tiny fp32 sliding case)
+with its own roofline block, its error against the CPU oracle and the oracle's time.
 
 value = algorithmic KV bytes read by decode attention per step / wall time per step (GB/s),
 with the timed steps replayed as one HIP graph of exactly that many consecutive steps (a
-serving loop replays one graph per iteration over all its layers).  Inputs are
-resident in HBM; the caches are rotated over several copies so that the 256 MB last-level
-cache cannot hold a step's working set.  The roofline figure times the attention call alone:
-back-to-back calls between two HIP events on the launch stream.
+serving loop replays one graph per iteration over all its layers).  Inputs are resident in HBM;
+the caches rotate over copies so that the 256 MB last-level cache cannot hold a step's working
+set.  The roofline figure times the attention call alone: back-to-back calls between two HIP
+events on the launch stream.
+
+--only NAME runs just one workload's timed calls (for counter runs under rocprofv3).
 """
 from __future__ import annotations
 
@@ -20,7 +23,6 @@ import argparse
 import dataclasses
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -37,35 +39,46 @@ import workloads as wl  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
 BS = wl.BLOCK_SIZE
+HEADLINE = "kv_shared_decode_bf16"
+MFMA_FLOP = 16 * 16 * 32 * 2   # one v_mfma_f32_16x16x32_bf16
 
-
-# Sources of the decode kernels: the HBM traffic recorded under profiles/ applies only while
-# their hash is unchanged.
+# Kernel sources behind each committed counter record: a record applies only while the sha256
+# of its sources is unchanged (bench.py reports null otherwise).
 DECODE_SOURCES = ("decode.hip", "attn_common.hpp", "device_common.hpp", "launch.hpp")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_stream_kernel.softcap_decode_bf16.pmc.md")
+PREFILL_SOURCES = ("prefill.hip", "prefill_common.hpp", "attn_common.hpp", "device_common.hpp",
+                   "launch.hpp")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
-def decode_sources_sha256():
+def sources_sha256(files):
     h = hashlib.sha256()
-    for f in DECODE_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "paged_kv_cache_write_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def recorded_traffic():
-    """HBM bytes per attn_decode call of the headline workload from the committed counter
-    summary (FETCH_SIZE and WRITE_SIZE, each scaled by the copy-kernel calibration), or None
-    when there is none or the decode sources changed since it was taken."""
+def counter_record(name, files):
+    """The JSON record of a committed counter summary under profiles/, or None when there is
+    none or its kernel sources changed since it was taken."""
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(os.path.join(PROFILES, name)).read()
     except OSError:
+        return None
+    if "```json" not in text:
         return None
     blob = text[text.index("```json") + 7:]
     rec = json.loads(blob[:blob.index("```")])
-    if rec.get("sources_sha256") != decode_sources_sha256():
+    if rec.get("sources_sha256") != sources_sha256(files):
         return None
-    return float(rec["hbm_bytes_per_call"])
+    return rec
+
+
+def decode_traffic(workload):
+    """HBM bytes per attn_decode call of a decode workload from its committed FETCH_SIZE /
+    WRITE_SIZE record (each scaled by the copy-kernel calibration), or None."""
+    rec = counter_record(f"decode_stream_kernel.{workload}.pmc.md", DECODE_SOURCES)
+    return None if rec is None else float(rec["hbm_bytes_per_call"])
 
 
 def copy_probe(mib):
@@ -83,16 +96,20 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def params(spec):
+def params(spec, kv_norm_w=None):
     return ga.layer_params(spec.dtype, spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
                            window=spec.window, scale=spec.scale, softcap=spec.softcap,
                            k_eq_v=spec.k_eq_v, rope_theta=spec.rope_theta, rms_eps=spec.rms_eps,
                            rope_angles=spec.rope_angles, rope_scale=spec.rope_scale,
-                           page_ring=spec.page_ring)
+                           page_ring=spec.page_ring, kv_norm_w=kv_norm_w)
 
 
 def i32(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+
+def f32(x):
+    return float(np.float32(x))
 
 
 # ----------------------------------------------------------------------------- work models ---
@@ -127,6 +144,47 @@ def prefill_flops(spec, lens, news):
     return total * spec.num_q_heads * 4 * spec.head_dim
 
 
+def write_bytes(spec, T, with_q=True):
+    """Algorithmic bytes of one ga_kv_cache_write: every row read once and written once."""
+    e = 2 if spec.dtype == "bf16" else 4
+    rows = (spec.num_q_heads if with_q else 0) + spec.num_kv_heads * (1 if spec.k_eq_v else 2)
+    return 2 * T * rows * spec.head_dim * e
+
+
+# ----------------------------------------------------------------------------- oracle ---------
+
+def err_stats(got: torch.Tensor, ref: np.ndarray):
+    g = got.float().cpu().numpy().astype(np.float64)
+    e = np.abs(g - ref)
+    return {"max_abs": float(f"{e.max():.4g}"), "mean_abs": float(f"{e.mean():.4g}")}
+
+
+def window_pages(kc, vc, pb, spec, lens):
+    """Host copies (oracle storage) of only the pages each sequence's decode query reads, with
+    a block table renumbered to match; logical page indices (and so the K page layout) are
+    kept, entries before the window point at compact page 0 and are never read."""
+    ids, bt = [], np.zeros_like(pb.block_table)
+    for b, L in enumerate(lens):
+        lo = max(0, int(L) - spec.window) if spec.window > 0 else 0
+        for p in range(lo // BS, (int(L) - 1) // BS + 1):
+            bt[b, p] = len(ids)
+            ids.append(int(pb.block_table[b, p]))
+    idx = torch.tensor(ids, dtype=torch.long, device=kc.device)
+    kh = wl.to_numpy_bits(kc.index_select(0, idx))
+    vh = None if vc is None else wl.to_numpy_bits(vc.index_select(0, idx))
+    return kh, vh, bt
+
+
+def timed(fn, reps):
+    """(median seconds, result of the last run) of `reps` runs of fn()."""
+    ts, r = [], None
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        r = fn()
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts)), r
+
+
 # ----------------------------------------------------------------------------- set-up ---------
 
 class DecodeBench:
@@ -136,17 +194,14 @@ class DecodeBench:
 
     def __init__(self, name, copies, dev, seed=0, exact=False):
         specs, pb = wl.workload(name)
-        self.name, self.spec, self.pb, self.dev = name, specs[0], pb, dev
+        self.name, self.spec, self.pb, self.dev, self.exact = name, specs[0], pb, dev, exact
         s = self.spec
         if exact:
             ws = wl.norm_weights(dataclasses.replace(s, k_eq_v=False), seed)
             self.w = [ws[0].to(dev), ws[1].to(dev), None]
             self.spec = s = dataclasses.replace(s, k_eq_v=2, rope_angles=64)
             self.kvw = (self.w[1], ws[2].to(dev))
-            self.p = ga.layer_params(s.dtype, s.num_q_heads, s.num_kv_heads, s.head_dim,
-                                     window=s.window, scale=s.scale, softcap=s.softcap, k_eq_v=2,
-                                     rope_theta=s.rope_theta, rms_eps=s.rms_eps,
-                                     rope_angles=s.rope_angles, kv_norm_w=self.kvw)
+            self.p = params(s, self.kvw)
         else:
             self.p = params(s)
             self.w = [None if x is None else x.to(dev) for x in wl.norm_weights(s, seed)]
@@ -175,15 +230,13 @@ class DecodeBench:
 
     def _write_past(self, kc, vc, past, seed):
         s, dev = self.spec, self.dev
-        B = len(past)
         chunk = 4096
-        start = np.zeros(B, np.int64)
+        start = np.zeros(len(past), np.int64)
         while (start < past).any():
             n = np.minimum(past - start, chunk).astype(np.int32)
             cl = (start + n).astype(np.int32)
             cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
-            T = int(cu[-1])
-            _, k, v = wl.raw_qkv(s, T, seed + 1000 + int(start.max()), device=dev)
+            _, k, v = wl.raw_qkv(s, int(cu[-1]), seed + 1000 + int(start.max()), device=dev)
             ga.kv_cache_write(self.p, None, k, v, *self.w, i32(cu, dev), i32(cl, dev), self.bt,
                               kc, vc)
             start = start + n
@@ -199,9 +252,28 @@ class DecodeBench:
         ga.attn_decode(self.p, self.q, self.kcs[c], self.vcs[c], self.bt, self.cl, self.max_len,
                        out=self.out, workspace=self.ws)
 
+    def oracle_check(self, reps):
+        """The oracle's decode over the same stored q̂ and cache bytes (cache copy 0): the
+        GPU output's error, and the oracle's median wall time over `reps` runs on the host's
+        cores.  (The exact K=V form is checked against the oracle by the test-suite only.)"""
+        import oracle
+        assert self.spec.k_eq_v != 2
+        s, pb = self.spec, self.pb
+        self.write(0)
+        self.attend(0)
+        torch.cuda.synchronize()
+        lens = pb.context_lens
+        kc, vc, bt = window_pages(self.kcs[0], self.vcs[0], pb, s, lens)
+        q = wl.to_numpy_bits(self.q)
+        code = oracle.BF16 if s.dtype == "bf16" else oracle.FP32
+        sec, ref = timed(lambda: oracle.attn_decode(
+            code, s.num_q_heads, s.num_kv_heads, s.head_dim, s.window, f32(s.scale),
+            f32(s.softcap), int(s.k_eq_v), q, kc, vc, bt, lens), reps)
+        return err_stats(self.out, ref), sec
+
 
 class PrefillBench:
-    """The 6-layer chunked-prefill stack: per layer a write of the 4 x 2048 chunk + prefill."""
+    """The 6-layer chunked-prefill stack: per layer a write of the varlen chunk + prefill."""
 
     def __init__(self, dev, seed=0):
         specs, pb = wl.workload("chunked_prefill_bf16")
@@ -225,7 +297,8 @@ class PrefillBench:
             self.layers.append(dict(p=p, w=w, kc=kc, vc=vc, q=q, k=k, v=v, out=out, spec=s))
             del kp, vp
         torch.cuda.synchronize()
-        self.flops = sum(prefill_flops(s, lens, news) for s in specs)
+        self.layer_flops = [prefill_flops(s, lens, news) for s in specs]
+        self.flops = sum(self.layer_flops)
         self.max_q = int(news.max())
 
     def write(self, li):
@@ -237,6 +310,103 @@ class PrefillBench:
         L = self.layers[li]
         ga.attn_prefill(L["p"], L["q"], self.cu, L["kc"], L["vc"], self.bt, self.cl, self.max_q,
                         out=L["out"])
+
+    def oracle_check(self, rows_per_seq):
+        """Sampled rows of the first sliding layer and of the global layer against the oracle
+        over the stored bytes (q̂ and caches after the timed write): the GPU's error, and the
+        oracle's wall time per row on the host's cores, which extrapolates to the whole stack
+        (every row of a sliding layer sees 1024 keys; random rows sample the global layer's mix
+        of key counts)."""
+        import oracle
+        pb = self.pb
+        rng = np.random.default_rng(7)
+        cu = pb.cu_seqlens
+        res = {}
+        for li in (0, len(self.layers) - 1):
+            L, s = self.layers[li], self.layers[li]["spec"]
+            # q is normalised and rotated in place by the write, so write once from the raw
+            # projection again before attending
+            q_raw, _, _ = wl.raw_qkv(s, pb.total_new, 600 + li, device=self.dev)
+            L["q"].copy_(q_raw)
+            self.write(li)
+            self.attend(li)
+            torch.cuda.synchronize()
+            rows = np.sort(np.concatenate([
+                cu[b] + rng.choice(int(pb.n_new[b]), size=rows_per_seq[li != 0], replace=False)
+                for b in range(pb.batch)])).astype(np.int32)
+            kc = wl.to_numpy_bits(L["kc"])
+            vc = wl.to_numpy_bits(L["vc"])
+            q = wl.to_numpy_bits(L["q"])
+            t0 = time.perf_counter()
+            ref = oracle.attention(oracle.BF16, s.num_q_heads, s.num_kv_heads, s.head_dim,
+                                   s.window, f32(s.scale), f32(s.softcap), int(s.k_eq_v), q, cu,
+                                   kc, vc, pb.block_table, pb.context_lens, rows=rows)
+            sec = time.perf_counter() - t0
+            res["sliding" if li == 0 else "global"] = dict(
+                rows=len(rows), seconds=sec, err=err_stats(L["out"][rows], ref[rows]))
+        n_sl = len(self.layers) - 1
+        full = (res["sliding"]["seconds"] / res["sliding"]["rows"] * pb.total_new * n_sl +
+                res["global"]["seconds"] / res["global"]["rows"] * pb.total_new)
+        return res, full
+
+
+class TinyBench:
+    """The tiny fp32 sliding case: one sequence, a 256-token prefill (write + attention), then
+    16 single-token decode steps (write + attention)."""
+
+    def __init__(self, dev, seed=1):
+        specs, pb = wl.workload("tiny_sliding_fp32")
+        self.spec, self.pb, self.dev = specs[0], pb, dev
+        s = self.spec
+        self.p = params(s)
+        self.w = [x.to(dev) for x in wl.norm_weights(s, seed)]
+        self.bt = i32(pb.block_table, dev)
+        self.kc, self.vc = wl.empty_caches(s, pb.num_blocks, dev)
+        self.q, self.k, self.v = wl.raw_qkv(s, 256, seed, device=dev)
+        self.steps = [wl.raw_qkv(s, 1, 100 + i, device=dev) for i in range(16)]
+        self.cu0, self.cl0 = i32([0, 256], dev), i32([256], dev)
+        self.cu1 = i32([0, 1], dev)
+        self.cls = [i32([257 + i], dev) for i in range(16)]
+        self.qs = [None] * 16
+        self.outs = [None] * 17
+
+    def run(self):
+        """The whole case once, q̂ and outputs kept for the oracle."""
+        self.qp = self.q.clone()
+        ga.kv_cache_write(self.p, self.qp, self.k, self.v, *self.w, self.cu0, self.cl0, self.bt,
+                          self.kc, self.vc)
+        self.outs[0] = ga.attn_prefill(self.p, self.qp, self.cu0, self.kc, self.vc, self.bt,
+                                       self.cl0, 256)
+        for i, (q, k, v) in enumerate(self.steps):
+            self.qs[i] = q.clone()
+            ga.kv_cache_write(self.p, self.qs[i], k, v, *self.w, self.cu1, self.cls[i], self.bt,
+                              self.kc, self.vc)
+            self.outs[i + 1] = ga.attn_decode(self.p, self.qs[i], self.kc, self.vc, self.bt,
+                                              self.cls[i], 257 + i)
+
+    def oracle_check(self, reps):
+        """Every output against the oracle over the stored bytes (the cache after all 16 steps
+        holds the same bytes at every position each call read); median oracle time of the
+        whole case."""
+        import oracle
+        s, pb = self.spec, self.pb
+        torch.cuda.synchronize()
+        kc, vc = wl.to_numpy_bits(self.kc), wl.to_numpy_bits(self.vc)
+        qp = wl.to_numpy_bits(self.qp)
+        qs = [wl.to_numpy_bits(q) for q in self.qs]
+
+        def case():
+            r = [oracle.attention(oracle.FP32, 4, 2, 256, 128, 1.0, 0.0, 0, qp,
+                                  np.array([0, 256], np.int32), kc, vc, pb.block_table,
+                                  np.array([256], np.int32))]
+            for i in range(16):
+                r.append(oracle.attn_decode(oracle.FP32, 4, 2, 256, 128, 1.0, 0.0, 0, qs[i], kc,
+                                            vc, pb.block_table, np.array([257 + i], np.int32)))
+            return r
+        sec, refs = timed(case, reps)
+        errs = [np.abs(o.float().cpu().numpy().astype(np.float64) - r).max()
+                for o, r in zip(self.outs, refs)]
+        return {"max_abs": float(f"{max(errs):.4g}")}, sec
 
 
 def prefill_global_kv_forms(pf: "PrefillBench", reps: int):
@@ -254,11 +424,7 @@ def prefill_global_kv_forms(pf: "PrefillBench", reps: int):
         s = dataclasses.replace(base, k_eq_v=2 if exact else True,
                                 rope_angles=64 if exact else 0)
         ws = [x.to(dev) for x in wl.norm_weights(dataclasses.replace(s, k_eq_v=False), 70)]
-        p = ga.layer_params(s.dtype, s.num_q_heads, s.num_kv_heads, s.head_dim, window=s.window,
-                            scale=s.scale, softcap=s.softcap, k_eq_v=s.k_eq_v,
-                            rope_theta=s.rope_theta, rms_eps=s.rms_eps,
-                            rope_angles=s.rope_angles,
-                            kv_norm_w=(ws[1], ws[2]) if exact else None)
+        p = params(s, (ws[1], ws[2]) if exact else None)
         kc, _ = wl.empty_caches(s, pb.num_blocks, dev)
         _, kp, _ = wl.raw_qkv(s, int(past.sum()), 71, device=dev)
         ga.kv_cache_write(p, None, kp, None, None, ws[1], None, cu_past, i32(past, dev), pf.bt,
@@ -359,27 +525,136 @@ def copy_bandwidth(dev, nbytes=1 << 30, reps=10):
     return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
 
 
-def cpu_baseline_decode(db: DecodeBench, budget_s: float):
-    """The oracle on the host cores, over the same decode batch (the cache copied back)."""
-    import oracle
-    s, pb = db.spec, db.pb
-    kc = wl.to_numpy_bits(db.kcs[0])
-    vc = None if db.vcs[0] is None else wl.to_numpy_bits(db.vcs[0])
-    q = wl.to_numpy_bits(db.q)
-    code = oracle.BF16 if s.dtype == "bf16" else oracle.FP32
-    runs, t_total = 0, 0.0
-    while t_total < budget_s:
-        t0 = time.perf_counter()
-        oracle.attn_decode(code, s.num_q_heads, s.num_kv_heads, s.head_dim, s.window,
-                           float(np.float32(s.scale)), float(np.float32(s.softcap)),
-                           int(s.k_eq_v), q, kc, vc, pb.block_table, pb.context_lens)
-        t_total += time.perf_counter() - t0
-        runs += 1
-    return dict(value=round(db.bytes * runs / t_total / 1e9, 4), unit="GB/s",
-                cores=oracle.num_threads(), kind="oracle",
-                sample=f"{runs} full passes of the oracle's decode attention over the same "
-                       f"{pb.batch}-sequence batch ({db.bytes / 1e9:.3f} GB of K/V each), "
-                       f"{t_total:.1f} s total")
+def hbm_block(nbytes, call_ms, traffic, kernel):
+    gbs = nbytes / (call_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "traffic_unit": "HBM bytes per call", "bytes_per_call": nbytes,
+            "call_us": round(call_ms * 1e3, 2)}
+
+
+# ----------------------------------------------------------------------------- workloads -----
+
+def run_decode(name, dev, args, copies, exact=False, oracle_reps=0):
+    """Step (write + decode, graph-replayed), attention call and write call times of one decode
+    workload; with oracle_reps > 0 also its error against the oracle and the oracle's time."""
+    db = DecodeBench(name, copies, dev, exact=exact)
+    n = len(db.kcs)
+    wall = time_chain(lambda i: (db.write(i), db.attend(i)), n, args.steps, args.warmup)
+    a_ms = time_calls(db.attend, n, args.steps, args.warmup)
+    w_ms = time_calls(db.write, n, args.steps, args.warmup)
+    pct = call_percentiles(db.attend, n, max(args.steps, 20), args.warmup)
+    tag = name + ("_exact" if exact else "")
+    traffic = decode_traffic(tag)
+    kern = "attn_decode (decode_stream_kernel + decode_merge_kernel)"
+    res = {"roofline": hbm_block(db.bytes, a_ms, traffic, kern),
+           "step_us": round(wall * 1e3, 2),
+           "step_GBps": round(db.bytes / (wall * 1e-3) / 1e9, 1),
+           "write_call_us": round(w_ms * 1e3, 2),
+           "write_GBps": round(write_bytes(db.spec, db.pb.batch) / (w_ms * 1e-3) / 1e9, 1),
+           "call_us_p10_p50_p90": pct}
+    log(f"{tag}: attention call {a_ms * 1e3:.1f} us -> {res['roofline']['achieved']:.0f} GB/s "
+        f"({res['roofline']['frac']:.1%}); step {wall * 1e3:.1f} us; write {w_ms * 1e3:.1f} us")
+    if oracle_reps and not exact:
+        err, sec = db.oracle_check(oracle_reps)
+        res["err_vs_oracle"] = err
+        res["oracle"] = {"seconds": round(sec, 3), "GBps": round(db.bytes / sec / 1e9, 4),
+                         "runs": oracle_reps, "sample": "the whole call"}
+        log(f"{tag}: vs oracle max {err['max_abs']:.3e} mean {err['mean_abs']:.3e}; oracle "
+            f"{sec:.2f} s")
+    return db, wall, res
+
+
+def run_prefill(dev, args, with_oracle):
+    pf = PrefillBench(dev)
+    nl = len(pf.layers)
+
+    def stack(i):
+        for li in range(nl):
+            pf.write(li)
+            pf.attend(li)
+    wall_p = time_chain(stack, 1, max(args.steps // 5, 3), max(args.warmup // 5, 1))
+    a_layers = [time_calls(lambda i, li=li: pf.attend(li), 1, 10, 3) for li in range(nl)]
+    w_layers = [time_calls(lambda i, li=li: pf.write(li), 1, 10, 3) for li in range(nl)]
+    attn_ms = float(sum(a_layers))
+    tf = pf.flops / (attn_ms * 1e-3) / 1e12
+    log(f"chunked_prefill: 6-layer attention {attn_ms:.3f} ms -> {tf:.1f} TFLOP/s "
+        f"({tf / BF16_PEAK_TFLOPS:.1%}); writes {sum(w_layers):.3f} ms; step {wall_p:.3f} ms")
+    rec = counter_record("prefill_tiled_kernel.chunked_prefill_bf16.pmc.md", PREFILL_SOURCES)
+    wb = sum(write_bytes(s, pf.pb.total_new) for s in pf.specs)
+    res = {"roofline": {"bound": "mfma", "kernel": "attn_prefill (prefill_tiled_kernel), 6 "
+                        "layers", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                        "traffic": None, "flops": pf.flops,
+                        "mfma_flop_ratio": None if rec is None else rec["mfma_flop_ratio"]},
+           "layers": nl, "attn_ms": round(attn_ms, 4),
+           "per_layer_attn_ms": [round(x, 4) for x in a_layers],
+           "per_layer_TFLOPs": [round(f / (ms * 1e-3) / 1e12, 1)
+                                for f, ms in zip(pf.layer_flops, a_layers)],
+           "write_ms": round(float(sum(w_layers)), 4),
+           "per_layer_write_ms": [round(x, 4) for x in w_layers],
+           "write_GBps": round(wb / (sum(w_layers) * 1e-3) / 1e9, 1),
+           "step_ms": round(wall_p, 4),
+           "step_TFLOPs": round(pf.flops / (wall_p * 1e-3) / 1e12, 2),
+           "chunks": {"n_new": pf.pb.n_new.tolist(), "past": pf.pb.past.tolist()}}
+    gflops = pf.layer_flops[-1]
+    forms = prefill_global_kv_forms(pf, 3)
+    for form, ms in forms.items():
+        log(f"chunked_prefill global layer, {form}: {ms:.3f} ms -> "
+            f"{gflops / (ms * 1e-3) / 1e12:.1f} TFLOP/s")
+    res["global_layer_kv_forms_ms"] = {"separate_v": round(a_layers[-1], 4),
+                                       **{f: round(ms, 4) for f, ms in forms.items()}}
+    if with_oracle:
+        o, full = pf.oracle_check((32, 8))
+        res["err_vs_oracle"] = {k: v["err"] for k, v in o.items()}
+        res["oracle"] = {"seconds_extrapolated": round(full, 1),
+                         "TFLOPs": round(pf.flops / full / 1e12, 6),
+                         "sample": f"{o['sliding']['rows']} random rows of a sliding layer "
+                                   f"({o['sliding']['seconds']:.2f} s) and {o['global']['rows']} "
+                                   f"of the global layer ({o['global']['seconds']:.2f} s), "
+                                   f"scaled by rows to the whole 6-layer stack"}
+        log(f"chunked_prefill vs oracle: {res['err_vs_oracle']}; oracle extrapolated "
+            f"{full:.0f} s")
+    del pf
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_tiny(dev, with_oracle):
+    tb = TinyBench(dev)
+    tb.run()
+    torch.cuda.synchronize()
+    s = tb.spec
+    pre_ms = time_calls(lambda i: ga.attn_prefill(tb.p, tb.qp, tb.cu0, tb.kc, tb.vc, tb.bt,
+                                                  tb.cl0, 256), 1, 20, 3)
+    dec_ms = time_calls(lambda i: ga.attn_decode(tb.p, tb.qs[15], tb.kc, tb.vc, tb.bt,
+                                                 tb.cls[15], 272), 1, 20, 3)
+    res = {"prefill_call_us": round(pre_ms * 1e3, 2), "decode_call_us": round(dec_ms * 1e3, 2),
+           "bound": "latency (one sequence, 256 queries then 16 single decodes)"}
+    if with_oracle:
+        err, sec = tb.oracle_check(3)
+        res["err_vs_oracle"] = err
+        res["oracle"] = {"seconds": round(sec, 4), "runs": 3,
+                         "sample": "the whole case (prefill + 16 decodes)"}
+    log(f"tiny_sliding_fp32: prefill {pre_ms * 1e3:.1f} us, decode {dec_ms * 1e3:.1f} us; "
+        f"{res.get('err_vs_oracle')}")
+    del tb
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_only(name, dev, args):
+    """Only the timed calls of one workload (for counter runs): set-up, then `steps` attention
+    calls (and, for the prefill stack, writes)."""
+    if name == "chunked_prefill_bf16":
+        pf = PrefillBench(dev)
+        for li in range(len(pf.layers)):
+            time_calls(lambda i, li=li: pf.attend(li), 1, args.steps, 1)
+        return {"only": name}
+    exact = name.endswith("_exact")
+    db = DecodeBench(name[:-6] if exact else name, 2, dev, exact=exact)
+    ms = time_calls(db.attend, len(db.kcs), args.steps, args.warmup)
+    return {"only": name, "attn_call_us": round(ms * 1e3, 2), "bytes_per_call": db.bytes}
 
 
 def main():
@@ -387,10 +662,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--copies", type=int, default=4, help="cache copies rotated over steps")
+    ap.add_argument("--copies", type=int, default=2, help="cache copies rotated over steps")
     ap.add_argument("--no-extra", action="store_true", help="headline decode workload only")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="no oracle runs (no cpu_baseline, no error figures)")
+    ap.add_argument("--only", default=None, metavar="WORKLOAD",
+                    help="only one workload's timed calls (counter runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB three times (counter calibration)")
     args = ap.parse_args()
@@ -403,21 +680,22 @@ def main():
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return
+    if args.only:
+        print(json.dumps(run_only(args.only, dev, args)), flush=True)
+        return
+    with_oracle = not args.no_cpu_baseline
 
-    # ---- headline: soft-capped decode -------------------------------------------------
-    head = DecodeBench("softcap_decode_bf16", args.copies, dev)
-    nc = len(head.kcs)
-    wall = time_chain(lambda i: (head.write(i), head.attend(i)), nc, args.steps, args.warmup)
-    a_ms = time_calls(head.attend, nc, args.steps, args.warmup)
-    w_ms = time_calls(head.write, nc, args.steps, args.warmup)
-    pct = call_percentiles(head.attend, nc, max(args.steps, 20), args.warmup)
-    copy_gbs = copy_bandwidth(dev)
+    # ---- headline: the global-layer K=V decode -------------------------------------------
+    head, wall, hres = run_decode(HEADLINE, dev, args, args.copies, oracle_reps=0)
     props = torch.cuda.get_device_properties(dev)
     value = head.bytes / (wall * 1e-3) / 1e9
-    achieved = head.bytes / (a_ms * 1e-3) / 1e9
-    log(f"softcap_decode: step {wall * 1e3:.1f} us ({args.steps} steps in one graph); "
-        f"attention call {a_ms * 1e3:.1f} us -> {achieved:.0f} GB/s; "
-        f"write call {w_ms * 1e3:.1f} us; {value:.0f} GB/s per step")
+    roof = dict(hres["roofline"])
+    roof.update({"call_us_p10_p50_p90": hres["call_us_p10_p50_p90"],
+                 "write_call_us": hres["write_call_us"],
+                 "peak_source": "MI355X published HBM3E bandwidth, 8 TB/s",
+                 "measured_copy_GBps": copy_bandwidth(dev),
+                 "device": {"name": props.name, "compute_units": props.multi_processor_count}})
+    pb = head.pb
     result = {
         "metric": "decode attn KV GB/s (% HBM peak); prefill attn TFLOP/s (% MFMA peak)",
         "value": round(value, 2),
@@ -431,79 +709,45 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "softcap_decode_bf16", "batch": head.pb.batch,
-                   "context_lens": "U[512,4096] seeded", "num_q_heads": 8, "num_kv_heads": 4,
-                   "head_dim": 256, "softcap": 50.0, "scale": 0.0625, "block_size": BS,
-                   "step": "kv_cache_write(32 new tokens) + attn_decode; the timed steps "
-                           "replayed as one HIP graph, each over the next cache copy",
-                   "kv_bytes_per_step": head.bytes, "cache_copies_rotated": nc,
+        "config": {"workload": HEADLINE, "batch": pb.batch,
+                   "context_lens": "U[29491, 36044] seeded", "num_q_heads": 32,
+                   "num_kv_heads": 4, "head_dim": 512, "k_eq_v": 1, "rope_theta": 1e6,
+                   "scale": 1.0, "block_size": BS,
+                   "step": "kv_cache_write(16 new tokens: q/k norm + RoPE, keys stored once) + "
+                           "attn_decode; the timed steps replayed as one HIP graph, each over "
+                           "the next cache copy",
+                   "kv_bytes_per_step": head.bytes, "cache_copies_rotated": len(head.kcs),
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "attn_decode (decode_stream_kernel + "
-                     "decode_merge_kernel)",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
-                     "traffic_unit": "HBM bytes per attn_decode call",
-                     "call_us": round(a_ms * 1e3, 2), "bytes_per_call": head.bytes,
-                     "call_us_p10_p50_p90": pct,
-                     "write_call_us": round(w_ms * 1e3, 2),
-                     "peak_source": "MI355X published HBM3E bandwidth, 8 TB/s",
-                     "measured_copy_GBps": copy_gbs,
-                     "device": {"name": props.name, "compute_units": props.multi_processor_count}},
+        "roofline": roof,
     }
+    if with_oracle:
+        err, sec = head.oracle_check(3)
+        result["config"]["err_vs_oracle"] = err
+        import oracle
+        result["cpu_baseline"] = {
+            "value": round(head.bytes / sec / 1e9, 4), "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"median of 3 full passes of the oracle's decode attention over the same "
+                      f"{pb.batch}-sequence batch and stored bytes ({head.bytes / 1e9:.3f} GB of "
+                      f"K per pass, {sec:.2f} s each)"}
+        log(f"{HEADLINE}: vs oracle max {err['max_abs']:.3e} mean {err['mean_abs']:.3e}; "
+            f"oracle {sec:.2f} s")
+    del head
+    torch.cuda.empty_cache()
+
     if not args.no_extra:
         extra = {}
-        for name in ("sliding_decode_bf16", "kv_shared_decode_bf16",
-                     "kv_shared_decode_bf16_exact"):
-            exact = name.endswith("_exact")
-            base = name[:-len("_exact")] if exact else name
-            db = DecodeBench(base, 2 if base == "kv_shared_decode_bf16" else args.copies, dev,
-                             exact=exact)
-            n = len(db.kcs)
-            wall_x = time_chain(lambda i: (db.write(i), db.attend(i)), n,
-                                max(args.steps // 2, 5), max(args.warmup // 2, 2))
-            a_x = time_calls(db.attend, n, max(args.steps // 2, 5), max(args.warmup // 2, 2))
-            gbs = db.bytes / (a_x * 1e-3) / 1e9
-            log(f"{name}: attention call {a_x * 1e3:.1f} us -> {gbs:.0f} GB/s "
-                f"({gbs / HBM_PEAK_GBS:.1%}); step {wall_x * 1e3:.1f} us")
-            extra[name] = {"attn_call_us": round(a_x * 1e3, 2), "kv_bytes": db.bytes,
-                           "attn_GBps": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
-                           "step_us": round(wall_x * 1e3, 2),
-                           "step_GBps": round(db.bytes / (wall_x * 1e-3) / 1e9, 1)}
+        reps = 3 if with_oracle else 0
+        for name, copies, exact in (("softcap_decode_bf16", 4, False),
+                                    ("sliding_decode_bf16", 2, False),
+                                    (HEADLINE, 2, True)):
+            db, _, res = run_decode(name, dev, args, copies, exact=exact, oracle_reps=reps)
+            extra[name + ("_exact" if exact else "")] = res
             del db
             torch.cuda.empty_cache()
-        pf = PrefillBench(dev)
-        nl = len(pf.layers)
-
-        def stack(i):
-            for li in range(nl):
-                pf.write(li)
-                pf.attend(li)
-        wall_p = time_chain(stack, 1, max(args.steps // 5, 3), max(args.warmup // 5, 1))
-        a_layers = [time_calls(lambda i, li=li: pf.attend(li), 1, 3, 1) for li in range(nl)]
-        w_layers = [time_calls(lambda i, li=li: pf.write(li), 1, 3, 1) for li in range(nl)]
-        attn_ms = float(sum(a_layers))
-        tf = pf.flops / (attn_ms * 1e-3) / 1e12
-        log(f"chunked_prefill: 6-layer attention {attn_ms:.3f} ms -> {tf:.1f} TFLOP/s "
-            f"({tf / BF16_PEAK_TFLOPS:.1%}); writes {sum(w_layers):.3f} ms; step {wall_p:.3f} ms")
-        extra["chunked_prefill_bf16"] = {
-            "layers": nl, "attn_ms": round(attn_ms, 4), "write_ms": round(float(sum(w_layers)), 4),
-            "step_ms": round(wall_p, 4), "flops": pf.flops, "attn_TFLOPs": round(tf, 2),
-            "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
-            "per_layer_attn_ms": [round(x, 4) for x in a_layers],
-            "step_TFLOPs": round(pf.flops / (wall_p * 1e-3) / 1e12, 2)}
-        gflops = prefill_flops(pf.specs[-1], pf.pb.context_lens, pf.pb.n_new)
-        forms = prefill_global_kv_forms(pf, 3)
-        for form, ms in forms.items():
-            log(f"chunked_prefill global layer, {form}: {ms:.3f} ms -> "
-                f"{gflops / (ms * 1e-3) / 1e12:.1f} TFLOP/s")
-        extra["chunked_prefill_bf16"]["global_layer_kv_forms_ms"] = {
-            "separate_v": round(a_layers[-1], 4),
-            **{f: round(ms, 4) for f, ms in forms.items()}}
+        extra["chunked_prefill_bf16"] = run_prefill(dev, args, with_oracle)
+        extra["tiny_sliding_fp32"] = run_tiny(dev, with_oracle)
         result["extra"] = extra
-        del pf
-        torch.cuda.empty_cache()
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline_decode(head, args.cpu_budget)
     print(json.dumps(result), flush=True)
 
 

@@ -52,18 +52,29 @@ def test_prefill_flops_match_a_brute_force_count(W):
 
 
 def test_named_workloads_keep_their_size():
-    """The headline decode step reads 272 487 536 algorithmic bytes and the chunked-prefill stack
-    does 5 222 948 667 392 flops (the figures quoted with the committed measurements)."""
-    specs, pb = wl.workload("softcap_decode_bf16")
-    assert bench.decode_bytes(specs[0], pb.context_lens) == 272487536
+    """Algorithmic bytes per decode call and flops of the chunked-prefill stack (the figures
+    quoted with the committed measurements)."""
+    for name, nbytes in (("softcap_decode_bf16", 272487536), ("sliding_decode_bf16", 1076101120),
+                         (bench.HEADLINE, 2128252080)):
+        specs, pb = wl.workload(name)
+        assert bench.decode_bytes(specs[0], pb.context_lens) == nbytes, name
     specs, pb = wl.workload("chunked_prefill_bf16")
-    assert sum(bench.prefill_flops(s, pb.context_lens, pb.n_new) for s in specs) == 5222948667392
+    assert pb.n_new.sum() == 8192 and len(set(pb.n_new.tolist())) == 4  # varlen chunks
+    assert sum(bench.prefill_flops(s, pb.context_lens, pb.n_new) for s in specs) == 5087395250176
 
 
-def test_traffic_record_matches_the_decode_sources():
-    """The counter record that roofline.traffic reads was taken on the current decode sources
-    (bench.py reports null otherwise)."""
-    assert bench.recorded_traffic() is not None
+@pytest.mark.parametrize("workload", [bench.HEADLINE, "sliding_decode_bf16",
+                                      "softcap_decode_bf16"])
+def test_traffic_records_match_the_decode_sources(workload):
+    """The counter records that the roofline blocks' traffic reads were taken on the current
+    decode sources (bench.py reports null otherwise)."""
+    assert bench.decode_traffic(workload) is not None
+
+
+def test_prefill_counter_record_matches_the_prefill_sources():
+    rec = bench.counter_record("prefill_tiled_kernel.chunked_prefill_bf16.pmc.md",
+                               bench.PREFILL_SOURCES)
+    assert rec is not None and 1.0 <= rec["mfma_flop_ratio"] < 1.5
 
 
 def test_more_than_one_gpu_is_refused():
