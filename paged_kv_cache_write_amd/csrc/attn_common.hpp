@@ -83,12 +83,6 @@ struct KeqvLds {
   static constexpr int kElems = kPage * kStride;  // per wave
 };
 
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
-
 __device__ __forceinline__ int64_t clamp_blk(int64_t blk, int64_t nb) {
   if (blk < 0 || blk >= nb) {
     debug_flag(kDbgBlockId);

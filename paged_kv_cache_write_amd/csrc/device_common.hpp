@@ -164,6 +164,14 @@ __device__ __forceinline__ short4_t as_short4(const u32x2_t& v) {
   return __builtin_bit_cast(short4_t, v);
 }
 
+// LDS written by this wave is visible to this wave's later LDS reads (and its earlier reads
+// have completed): a wave-local barrier with workgroup-scope fences.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 // ------------------------------------------------------------------------ cross-lane -------
 
 __device__ __forceinline__ float xor_max(float v, int mask) {

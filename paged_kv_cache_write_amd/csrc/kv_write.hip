@@ -1,19 +1,37 @@
 // kv_write.hip -- fused RMSNorm + rotary embedding + paged scatter.
 //
-// A workgroup owns one token and a group of its head slots (q heads, then k heads, then v
-// heads).  Each wave issues the loads of its first rows before anything else (they depend only
-// on the token); then one parallel probe finds the owning sequence and its length, the
-// workgroup computes the token's rotation table -- cos and sin of t * omega_k for the D/2
-// frequencies, in double precision -- once into LDS, and each of its 4 wavefronts takes one
-// (token, head) row at a time.  Large batches give a workgroup all slots of its token;
-// small ones (a decode step) split a token's slots over several workgroups so that the launch
-// still fills the chip.  Each wave issues the loads of 4 rows before it processes the first.
-// With rotate-half RoPE the pair (k, k + D/2) must sit in one lane, so lane l holds the
-// C = D/128 consecutive elements starting at l*C of the first half and the matching C of the
-// second half.  The norm's sum of squares is a wavefront reduction; the norm and the rotation
-// run in double precision and the result is rounded once into the storage type (bf16:
-// round-to-odd to fp32, then to nearest even), so the stored cache does not depend on the
-// order of the arithmetic.
+// Every access to a row is one 16-byte unit per lane: with rotate-half RoPE the pair
+// (k, k + D/2) must meet in one lane, so a lane holds unit u of a row's first half
+// (elements uE .. uE+E-1, E = 16 / element size) and unit u of its second half; R = D / (2E)
+// lanes cover a row, and one wave instruction covers TT = 64 / R rows (4 at head size 256 in
+// bf16): a row group.
+//
+// A workgroup (4 waves) owns a tile of TT consecutive new tokens and a group of head slots
+// (q heads, then k heads, then v heads).  Row group g of the workgroup is one head slot for the
+// TT tokens of the tile, the tokens side by side.  So when the tokens are consecutive
+// positions of one sequence (a chunk), the lanes holding unit u of the TT rows write TT
+// consecutive rows of the same page column: the value elements of a transposed V page
+// ([d][16 rows]) merge into one request of 2 TT bytes instead of TT requests of 2 bytes, and
+// the K units ([unit column][16 rows]) into 16 TT contiguous bytes.  Large batches give a
+// workgroup all slots of its tile; small ones (a decode step) split them over several
+// workgroups so that the launch still fills the chip.
+//
+// Order of work in a workgroup: each wave issues the loads of its first row groups before
+// anything else (they depend only on the tile), then every row's R lanes find the sequence
+// owning the row's token by an R-ary search of cu_seqlens (one round of loads for up to R
+// sequences), which also fetches the owner's length, so the position is known after that
+// round; the row's block id load follows.  Meanwhile the workgroup computes the tile's rotation
+// table -- cos and sin of t * omega_k for its TT positions and the D/2 frequencies, formed and
+// evaluated in double precision -- and stages the norm weights, both in LDS; one barrier
+// publishes them.
+//
+// Precision: bf16 caches take the norm's scale 1/sqrt(mean(x^2) + eps) in fp32 (a relative
+// error of a few fp32 ulps, harmless to a bf16 result); the rotated pair x1 c - x2 s,
+// x2 c + x1 s is formed in double from the exact products x * w and the double table, because
+// when the two terms nearly cancel any fp32 rounding of them would be amplified in the small
+// result; the pair is then scaled in fp32 and rounded to bf16 (nearest even).  Every stored
+// value is within one ulp of the exact one and almost always equal to its correct rounding.
+// fp32 caches keep the whole norm + rotation in double and round once.
 //
 // Sources: [KUNLUN] = "Gemma 4 模型架构解析" (vLLM-Kunlun adaptation guide), §4.3 (a layer that
 // owns its cache norms k, rotates q and k, norms v), §6.3 (slot = page id * 16 + row), §6.4
@@ -21,6 +39,8 @@
 // Layout of the pages: K [blk][g] in 16-byte units, chunk-major, rows rotated by 4 on odd
 // logical pages and in unit columns with bit 3 set (k_page_elem); V [blk][g][d][row]
 // (transposed page).
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -42,7 +62,7 @@ struct KvWriteArgs {
   int64_t num_blocks;
   int32_t max_blocks, batch, total_tokens;
   int32_t Hq, Hkv, nslots, has_q, k_eq_v;
-  int32_t slots_per_wg, groups;  // head slots per workgroup; workgroups per token
+  int32_t slots_per_wg, groups;  // head slots per workgroup; workgroups per token tile
   double theta, eps, pos_scale;
   double log2_theta;  // log2(theta), formed on the host
   int32_t rope_angles;
@@ -50,240 +70,348 @@ struct KvWriteArgs {
   int32_t ring;    // block-table rows are rings of max_blocks pages
 };
 
-template <typename T>
-struct Elem;
-template <>
-struct Elem<float> {
-  static __device__ __forceinline__ double widen(float x) { return (double)x; }
-  static __device__ __forceinline__ void store(void* p, int64_t i, double x) {
-    ((float*)p)[i] = (float)x;  // round to nearest even
-  }
-};
-template <>
-struct Elem<uint16_t> {
-  static __device__ __forceinline__ double widen(uint16_t x) { return (double)bf16_to_f32(x); }
-  static __device__ __forceinline__ void store(void* p, int64_t i, double x) {
-    ((uint16_t*)p)[i] = f64_to_bf16(x);
-  }
+// Geometry of one row in 16-byte units.
+template <typename T, int D>
+struct Geo {
+  static constexpr int E = 16 / (int)sizeof(T);  // elements in one unit
+  static constexpr int H = D / 2;
+  static constexpr int R = H / E;                // lanes per row
+  static constexpr int TT = kWave / R;           // rows (tokens of a tile) per wave instruction
+  static_assert(R >= 1 && R <= kWave && kWave % R == 0, "row geometry");
 };
 
-// Store C consecutive elements (index i, a multiple of C, so the run is aligned) with one
-// store instruction: a lane's C elements of a half-row are consecutive in q and, inside one
-// 16-byte unit, in the K page.
-template <typename T, int C>
-__device__ __forceinline__ void store_run(void* p, int64_t i, const double (&x)[C]) {
-  if constexpr (sizeof(T) == 2 && C == 2) {
-    const uint32_t w = (uint32_t)f64_to_bf16(x[0]) | ((uint32_t)f64_to_bf16(x[1]) << 16);
-    *(uint32_t*)((uint16_t*)p + i) = w;
-  } else if constexpr (sizeof(T) == 2 && C == 4) {
-    const uint64_t w = (uint64_t)f64_to_bf16(x[0]) | ((uint64_t)f64_to_bf16(x[1]) << 16) |
-                       ((uint64_t)f64_to_bf16(x[2]) << 32) | ((uint64_t)f64_to_bf16(x[3]) << 48);
-    *(uint64_t*)((uint16_t*)p + i) = w;
-  } else if constexpr (sizeof(T) == 4 && C == 2) {
-    *(float2*)((float*)p + i) = make_float2((float)x[0], (float)x[1]);
-  } else if constexpr (sizeof(T) == 4 && C == 4) {
-    *(float4*)((float*)p + i) = make_float4((float)x[0], (float)x[1], (float)x[2], (float)x[3]);
+// Arithmetic type of the norm's scale: fp32 for bf16 storage, double for fp32.
+template <typename T>
+using Calc = std::conditional_t<sizeof(T) == 2, float, double>;
+
+constexpr int kRowGroupsInFlight = 4;  // row groups whose loads one wave keeps in flight
+
+// Unpack one 16-byte unit of storage elements into the arithmetic type.
+template <typename T>
+__device__ __forceinline__ void unpack(const u32x4_t& u, Calc<T> (&x)[16 / sizeof(T)]) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      x[2 * w] = bf16_lo(u[w]);
+      x[2 * w + 1] = bf16_hi(u[w]);
+    }
   } else {
 #pragma unroll
-    for (int e = 0; e < C; ++e) Elem<T>::store(p, i + e, x[e]);
+    for (int w = 0; w < 4; ++w) x[w] = (double)__uint_as_float(u[w]);
   }
 }
 
-constexpr int kRowsInFlight = 4;  // (token, head) rows whose loads one wave keeps in flight
-
-// One (token, head) row of q, k or v as this lane sees it: C elements of each half.
-template <typename T, int C>
-struct Row {
-  bool valid;
-  int kind, h;  // kind 0 = q, 1 = k, 2 = v
-  const T* src;
-  const float* w;
-  int64_t base;
-  T v1[C], v2[C];
-  __device__ __forceinline__ void locate(const KvWriteArgs& a, int slot, int64_t tok, int D) {
-    if (a.has_q && slot < a.Hq) { kind = 0; h = slot; }
-    else {
-      const int s = slot - (a.has_q ? a.Hq : 0);
-      if (s < a.Hkv) { kind = 1; h = s; } else { kind = 2; h = s - a.Hkv; }
-    }
-    src = (const T*)(kind == 0 ? (const void*)a.q : kind == 1 ? a.k : a.v);
-    w = kind == 0 ? a.wq : kind == 1 ? a.wk : a.wv;
-    const int heads = kind == 0 ? a.Hq : a.Hkv;
-    base = (tok * heads + h) * (int64_t)D;
-  }
-  template <int H>
-  __device__ __forceinline__ void load(int lane) {
+// Round into one 16-byte unit (nearest even, once).
+template <typename T>
+__device__ __forceinline__ u32x4_t pack(const Calc<T> (&x)[16 / sizeof(T)]) {
+  u32x4_t u;
+  if constexpr (sizeof(T) == 2) {
 #pragma unroll
-    for (int i = 0; i < C; ++i) {
-      v1[i] = src[base + lane * C + i];
-      v2[i] = src[base + H + lane * C + i];
+    for (int w = 0; w < 4; ++w)
+      u[w] = __builtin_bit_cast(uint32_t, cvt_bf16x2(x[2 * w], x[2 * w + 1]));
+  } else {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) u[w] = __float_as_uint((float)x[w]);
+  }
+  return u;
+}
+
+// Element e of a unit (as stored) for the transposed V page.
+template <typename T>
+__device__ __forceinline__ void store_elem(void* p, int64_t i, const u32x4_t& u, int e) {
+  if constexpr (sizeof(T) == 2) {
+    ((uint16_t*)p)[i] = (uint16_t)(u[e >> 1] >> (16 * (e & 1)));
+  } else {
+    ((uint32_t*)p)[i] = u[e];
+  }
+}
+
+// The sequence b owning token `tok` (cu[b] <= tok < cu[b + 1]) and the token's position t,
+// found by the R lanes of this lane's row (lanes R r .. R r + R - 1 of the wave), each row for
+// its own token: an R-ary search of the non-decreasing cu_seqlens in which every lane tests one
+// probe and the last probe at or below tok narrows the range R-fold.  The last round (probes
+// one apart) also fetches cu[b + 1] and each probe's length, so the position comes with the
+// owner.  Empty sequences never own a token: the last b with cu[b] <= tok is the non-empty
+// owner.  Returns -1 (for the row) when the metadata has no owner for tok or tok is past the
+// tokens of the call.  Every lane of the wave must call it (the rounds are wave-uniform).
+template <int R>
+__device__ __forceinline__ int find_owner(const KvWriteArgs& a, int64_t tok, int64_t& t) {
+  const int lane = threadIdx.x & 63, rl = lane % R, base = lane - rl;
+  int lo = 0, hi = tok < a.total_tokens ? a.batch : 0;  // the owner lies in [lo, hi)
+  int found = -1;
+  int64_t pos = 0;
+  // rounds: about log_R(batch), the same for every row (the bound depends on batch only)
+  for (;;) {
+    const bool active = found < 0 && hi - lo >= 1;
+    if (__ballot(active) == 0) break;
+    const int step = active ? (hi - lo + R - 1) / R : 1;
+    const int i = lo + rl * step;
+    const bool probe = active && i < hi;
+    int c0 = 0, c1 = 0, len = 0;
+    if (probe) {
+      c0 = a.cu[i];
+      if (step == 1) {
+        c1 = a.cu[i + 1];
+        len = a.ctx[i];
+      }
+    }
+    const uint64_t all = __ballot(probe && c0 <= tok);
+    const uint64_t mine = R == 64 ? all : (all >> base) & ((1ull << (R & 63)) - 1);
+    const int last = mine ? 63 - __builtin_clzll(mine) : 0;
+    const int c0s = __shfl(c0, base + last, kWave);
+    const int c1s = __shfl(c1, base + last, kWave);
+    const int lens = __shfl(len, base + last, kWave);
+    if (active) {
+      if (!mine) {
+        hi = lo;  // no probe at or below tok: no owner
+      } else if (step == 1) {
+        if (tok < c1s) {
+          found = lo + last;
+          pos = (int64_t)lens - (c1s - c0s) + (tok - c0s);
+        } else {
+          hi = lo;
+        }
+      } else {
+        lo = lo + last * step;
+        hi = lo + step < hi ? lo + step : hi;
+      }
     }
   }
-};
+  t = pos;
+  return found;
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
-  constexpr int C = D / 128;  // elements per lane in each half
-  constexpr int H = D / 2;
-  __shared__ double cos_t[H], sin_t[H];
+  using G = Geo<T, D>;
+  using C = Calc<T>;
+  constexpr int E = G::E, H = G::H, R = G::R, TT = G::TT;
+  constexpr int U = kRowGroupsInFlight;
+  // rotation tables, laid out [token][element e][unit u] (frequency k = uE + e) so that the
+  // lanes of a row read consecutive doubles; each token's table is padded by 16 doubles so
+  // that the tokens of a row group fall on different halves of the banks
+  constexpr int TS = H + 16;
+  __shared__ double cos_t[TT * TS], sin_t[TT * TS];
+  __shared__ float w_lds[3][D];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rr = lane / R, ul = lane % R;  // token of the tile (row of the group), unit
   // Workgroup ids are dealt to the 8 XCDs round robin; remap them so that each XCD takes a
-  // contiguous range of (token, slot group) items.  Consecutive tokens of a sequence share
-  // cache pages (16 rows of every 256-byte K column run and every 32-byte V row), so their
-  // partial-line stores then meet in one L2 and leave it as whole lines.  The grid is a
+  // contiguous range of (tile, slot group) items: neighbouring tiles share cache pages, so
+  // their partial-line stores meet in one L2 and leave it as whole lines.  The grid is a
   // multiple of 8, so the remap is a bijection; ids past the work return.
   const int64_t per_xcd = gridDim.x / 8;
   const int64_t item = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  const int64_t tok = item / a.groups;
-  const int group = (int)(item - tok * a.groups);
-  if (tok >= a.total_tokens) return;
-
-  // this wave's first kRowsInFlight rows are loaded before anything else: they depend only on
-  // the token, so their latency overlaps the sequence lookup and the rotation table
+  const int64_t tile = item / a.groups;
+  const int group = (int)(item - tile * a.groups);
+  const int64_t tok0 = tile * TT;
+  if (tok0 >= a.total_tokens) return;
+  const int64_t tok = tok0 + rr;  // this lane's token
+  const bool tok_ok = tok < a.total_tokens;
   const int s0 = group * a.slots_per_wg;
   const int s1 = s0 + a.slots_per_wg < a.nslots ? s0 + a.slots_per_wg : a.nslots;
-  constexpr int U = kRowsInFlight;
-  Row<T, C> rows[U];
-  auto load_rows = [&](int first) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int slot = first + 4 * u;
-      rows[u].valid = slot < s1;
-      if (rows[u].valid) rows[u].locate(a, slot, tok, D);
-      if (rows[u].valid) rows[u].template load<H>(lane);
+  const int ngroups = s1 - s0;  // row groups (head slots) of this workgroup
+
+  // this lane's row in row group g: head slot s0 + g of token tok
+  struct Row {
+    bool valid;
+    int kind, h;  // kind 0 = q, 1 = k, 2 = v
+    int64_t base;
+    u32x4_t u1, u2;
+  };
+  auto locate = [&](int g, Row& r) {
+    const int slot = s0 + g;
+    r.valid = g < ngroups && tok_ok;
+    const int sq = a.has_q ? a.Hq : 0;
+    if (slot < sq) { r.kind = 0; r.h = slot; }
+    else if (slot - sq < a.Hkv) { r.kind = 1; r.h = slot - sq; }
+    else { r.kind = 2; r.h = slot - sq - a.Hkv; }
+    const int heads = r.kind == 0 ? a.Hq : a.Hkv;
+    r.base = (tok * heads + r.h) * (int64_t)D;
+  };
+  auto load = [&](Row& r) {
+    if (r.valid) {
+      const T* src = (const T*)(r.kind == 0 ? (const void*)a.q : r.kind == 1 ? a.k : a.v);
+      r.u1 = *(const u32x4_t*)(src + r.base + ul * E);
+      r.u2 = *(const u32x4_t*)(src + r.base + H + ul * E);
     }
   };
-  load_rows(s0 + wave);
-
-  // sequence that owns this token: the b with cu[b] <= tok < cu[b + 1] (one parallel probe
-  // per sequence instead of a chain of dependent loads; empty sequences never match).  The
-  // probe also fetches the owner's context length, so the position is known after one round.
-  __shared__ int owner;
-  __shared__ int64_t own_t;
-  if (threadIdx.x == 0) owner = -1;
-  __syncthreads();
-  for (int i = threadIdx.x; i < a.batch; i += 256) {
-    const int c0 = a.cu[i], c1 = a.cu[i + 1], len = a.ctx[i];
-    if (c0 <= tok && tok < c1) {
-      owner = i;
-      own_t = (int64_t)len - (c1 - c0) + (tok - c0);
+  // the loads of this wave's first row groups go out before anything else
+  Row rows[U];
+#pragma unroll
+  for (int i = 0; i < U; ++i) {
+    locate(wave + 4 * i, rows[i]);
+    load(rows[i]);
+  }
+  // norm weights, staged in LDS (loaded now, stored after the owner search)
+  float wv_reg[3][2];
+  const float* wsrc[3] = {a.wq, a.wk, a.wv};
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int d = threadIdx.x + 256 * i;
+      wv_reg[k][i] = (wsrc[k] && d < D) ? wsrc[k][d] : 1.f;
     }
-  }
-  __syncthreads();
-  const int b = owner;
-  if (b < 0) {  // no sequence owns tok (cu_seqlens inconsistent)
-    debug_flag(kDbgOwner);
-    return;
-  }
-  const int64_t t = own_t;
-  const int64_t page = t >> 4;
-  if (t < 0) {  // inconsistent metadata (n_b > L_b): write nothing
-    debug_flag(kDbgLength);
-    return;
-  }
+
+  // the owning sequence, position and block of this lane's token
+  int64_t t = 0;
+  const int b = find_owner<R>(a, tok, t);
+  const bool pos_ok = b >= 0 && t >= 0;  // the row has a position (q needs nothing more)
+  if (tok_ok && b < 0) debug_flag(kDbgOwner);   // cu_seqlens inconsistent: the row is skipped
+  if (b >= 0 && t < 0) debug_flag(kDbgLength);  // n_b > L_b: skipped
+  const int64_t page = t >> 4, off = t & 15;
+  bool slot_ok = pos_ok;  // ... and a cache slot (k and v)
   int64_t blk = 0;
-  if (a.has_kv) {
-    if (!a.ring && page >= a.max_blocks) {  // (all the exits are workgroup-uniform)
+  if (a.has_kv && pos_ok) {
+    if (!a.ring && page >= a.max_blocks) {
       debug_flag(kDbgBound);
-      return;
+      slot_ok = false;
+    } else {
+      // the block id is checked after the rotation table, which its load latency overlaps
+      blk = a.bt[(int64_t)b * a.max_blocks + bt_col((int)page, a.max_blocks, a.ring)];
     }
-    // the block id is checked after the rotation table, which its load latency overlaps
-    blk = a.bt[(int64_t)b * a.max_blocks + bt_col((int)page, a.max_blocks, a.ring)];
   }
-  const int64_t off = t & 15;
 
-  // rotation table of position t ([KUNLUN] 挑战 5 proportional RoPE; [INFLM] follow-up list,
-  // linear scaling): omega_k = theta^(-2k/D) for k < rope_angles, 0 above; angle
-  // (t / pos_scale) * omega_k
+  // rotation tables of the tile's positions ([KUNLUN] 挑战 5 proportional RoPE; [INFLM]
+  // follow-up list, linear scaling): omega_k = theta^(-2k/D) for k < rope_angles, 0 above;
+  // angle (t / pos_scale) * omega_k, formed and evaluated in double.  Token j's position is
+  // held by lane R j of every wave (every wave computes the same owners).
   const bool rope = a.theta > 0.0;
   if (rope) {
-    const double tp = (double)t / a.pos_scale;
-    for (int k = threadIdx.x; k < H; k += 256) {
+    for (int q = threadIdx.x; q < TT * H; q += 256) {
+      const int j = q / H, k = q - j * H;
+      const int64_t tj = __shfl(t, R * j, kWave);
       double sn = 0.0, cs = 1.0;
       if (k < a.rope_angles) {
         // theta^(-2k/D) as exp2 of a product: within a few ulp of the power, like it
         const double omega = exp2(-((2.0 * k) / (double)D) * a.log2_theta);
-        sincos(tp * omega, &sn, &cs);
+        sincos((double)tj / a.pos_scale * omega, &sn, &cs);
       }
-      cos_t[k] = cs;
-      sin_t[k] = sn;
+      cos_t[j * TS + (k % E) * R + k / E] = cs;
+      sin_t[j * TS + (k % E) * R + k / E] = sn;
     }
   }
-  if (a.has_kv && (blk < 0 || blk >= a.num_blocks)) {  // no slot to write: nothing
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int d = threadIdx.x + 256 * i;
+      if (d < D) w_lds[k][d] = wv_reg[k][i];
+    }
+  if (a.has_kv && slot_ok && (blk < 0 || blk >= a.num_blocks)) {  // no slot: k/v skipped
     debug_flag(kDbgBlockId);
-    return;
+    slot_ok = false;
   }
   __syncthreads();
 
-  // the rows of this wave, kRowsInFlight at a time: all their loads are issued before the
-  // first row is processed
-  for (int first = s0 + wave; first < s1; first += 4 * U) {
-    if (first != s0 + wave) load_rows(first);
+  auto process = [&](const Row& r) {
+    const bool has_w = r.kind == 0 ? a.wq != nullptr : r.kind == 1 ? a.wk != nullptr
+                                                                    : a.wv != nullptr;
+    // keys are stored unrotated in the exact K=V form (k_eq_v = 2): the attention kernels
+    // rotate them for the scores and read them unrotated as values
+    const bool rot = rope && (r.kind == 0 || (r.kind == 1 && a.k_eq_v != 2));
+    C x1[E], x2[E];
+    unpack<T>(r.u1, x1);
+    unpack<T>(r.u2, x2);
+    // RMSNorm: the row's sum of squares over its R lanes (rows without a weight ignore it)
+    C ss = 0;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (!rows[u].valid) continue;
-      const Row<T, C>& r = rows[u];
-      double x1[C], x2[C];
+    for (int e = 0; e < E; ++e) ss += x1[e] * x1[e] + x2[e] * x2[e];
 #pragma unroll
-      for (int i = 0; i < C; ++i) {
-        x1[i] = Elem<T>::widen(r.v1[i]);
-        x2[i] = Elem<T>::widen(r.v2[i]);
-      }
-      if (r.w) {
-        double ss = 0.0;
+    for (int m = R / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, kWave);
+    C inv = 1;
+    if (has_w) {
+      if constexpr (sizeof(T) == 2) inv = rsqrtf(ss / (float)D + (float)a.eps);
+      else inv = 1.0 / sqrt(ss / D + a.eps);
+    }
+    const float* w = w_lds[r.kind];  // all ones when the tensor has no weight
+    const double* cj = cos_t + rr * TS + ul;  // element e at cj[e R]
+    const double* sj = sin_t + rr * TS + ul;
+    if constexpr (sizeof(T) == 2) {
+      if (rot) {
 #pragma unroll
-        for (int i = 0; i < C; ++i) ss += x1[i] * x1[i] + x2[i] * x2[i];
-        ss = wave_sum_f64(ss);
-        const double inv = 1.0 / sqrt(ss / D + a.eps);
-#pragma unroll
-        for (int i = 0; i < C; ++i) {
-          x1[i] = x1[i] * inv * (double)r.w[lane * C + i];
-          x2[i] = x2[i] * inv * (double)r.w[H + lane * C + i];
+        for (int e = 0; e < E; ++e) {
+          const double a1 = (double)x1[e] * (double)w[ul * E + e];  // exact products
+          const double a2 = (double)x2[e] * (double)w[H + ul * E + e];
+          const double cs = cj[e * R], sn = sj[e * R];
+          x1[e] = (float)(a1 * cs - a2 * sn) * inv;
+          x2[e] = (float)(a2 * cs + a1 * sn) * inv;
         }
-      }
-      // keys are stored unrotated in the exact K=V form (k_eq_v = 2): the attention kernels
-      // rotate them for the scores and read them unrotated as values
-      if (rope && (r.kind == 0 || (r.kind == 1 && a.k_eq_v != 2))) {
-#pragma unroll
-        for (int i = 0; i < C; ++i) {
-          const double cs = cos_t[lane * C + i], sn = sin_t[lane * C + i];
-          const double y1 = x1[i] * cs - x2[i] * sn;
-          const double y2 = x2[i] * cs + x1[i] * sn;
-          x1[i] = y1;
-          x2[i] = y2;
-        }
-      }
-      if (r.kind == 0) {
-        store_run<T, C>(a.q, r.base + lane * C, x1);
-        store_run<T, C>(a.q, r.base + H + lane * C, x2);
-      } else if (r.kind == 1) {
-        const int64_t pg = (blk * a.Hkv + r.h) * (int64_t)D * kPage;
-        store_run<T, C>(a.kc, pg + k_page_elem<sizeof(T)>((int)off, lane * C, page), x1);
-        store_run<T, C>(a.kc, pg + k_page_elem<sizeof(T)>((int)off, H + lane * C, page), x2);
       } else {
-        const int64_t pg = (blk * a.Hkv + r.h) * (int64_t)D * kPage;
 #pragma unroll
-        for (int i = 0; i < C; ++i) {
-          Elem<T>::store(a.vc, pg + (int64_t)(lane * C + i) * kPage + off, x1[i]);
-          Elem<T>::store(a.vc, pg + (int64_t)(H + lane * C + i) * kPage + off, x2[i]);
+        for (int e = 0; e < E; ++e) {
+          x1[e] = x1[e] * w[ul * E + e] * inv;
+          x2[e] = x2[e] * w[H + ul * E + e] * inv;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        x1[e] = x1[e] * inv * (double)w[ul * E + e];
+        x2[e] = x2[e] * inv * (double)w[H + ul * E + e];
+      }
+      if (rot) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const double cs = cj[e * R], sn = sj[e * R];
+          const double y1 = x1[e] * cs - x2[e] * sn;
+          const double y2 = x2[e] * cs + x1[e] * sn;
+          x1[e] = y1;
+          x2[e] = y2;
         }
       }
     }
+    const u32x4_t o1 = pack<T>(x1), o2 = pack<T>(x2);
+    if (r.kind == 0) {
+      *(u32x4_t*)((T*)a.q + r.base + ul * E) = o1;
+      *(u32x4_t*)((T*)a.q + r.base + H + ul * E) = o2;
+    } else {
+      const int64_t pg = (blk * a.Hkv + r.h) * (int64_t)D * kPage;
+      if (r.kind == 1) {
+        *(u32x4_t*)((T*)a.kc + pg + k_page_elem<sizeof(T)>((int)off, ul * E, page)) = o1;
+        *(u32x4_t*)((T*)a.kc + pg + k_page_elem<sizeof(T)>((int)off, H + ul * E, page)) = o2;
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          store_elem<T>(a.vc, pg + (int64_t)(ul * E + e) * kPage + off, o1, e);
+          store_elem<T>(a.vc, pg + (int64_t)(H + ul * E + e) * kPage + off, o2, e);
+        }
+      }
+    }
+  };
+
+  // the row groups of this wave, U at a time: all their loads are issued before the first is
+  // processed.  A row is valid for all its R lanes or for none, and the norm's shuffles stay
+  // inside a row, so the lanes of a skipped row skip it whole.  q rows need a position only;
+  // k and v rows need a cache slot as well.
+  for (int first = wave; first < ngroups; first += 4 * U) {
+    if (first != wave) {
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        locate(first + 4 * i, rows[i]);
+        load(rows[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < U; ++i)
+      if (rows[i].valid && (rows[i].kind == 0 ? pos_ok : slot_ok)) process(rows[i]);
   }
 }
 
 template <typename T, int D>
 hipError_t launch_t(KvWriteArgs a, hipStream_t s) {
+  using G = Geo<T, D>;
   if (a.total_tokens == 0 || a.nslots == 0) return hipSuccess;
-  // Slots per workgroup: all of a token's when there are enough tokens to fill the chip
-  // (about 2048 workgroups of 4 waves), otherwise down to one slot per wave.
-  const int64_t rows = (int64_t)a.total_tokens * a.nslots;
-  int64_t per_wave = (rows + 4 * 2048 - 1) / (4 * 2048);
+  // Slots per workgroup: all of a tile's when there are enough tiles to fill the chip (about
+  // 2048 workgroups of 4 waves), otherwise down to one row group per wave.
+  const int64_t tiles = ((int64_t)a.total_tokens + G::TT - 1) / G::TT;
+  const int64_t rgs = tiles * a.nslots;
+  int64_t per_wave = (rgs + 4 * 2048 - 1) / (4 * 2048);
   const int64_t max_per_wave = (a.nslots + 3) / 4;
   per_wave = per_wave < 1 ? 1 : (per_wave > max_per_wave ? max_per_wave : per_wave);
   a.slots_per_wg = (int)(4 * per_wave);
   a.groups = (a.nslots + a.slots_per_wg - 1) / a.slots_per_wg;
-  const int64_t blocks = ((int64_t)a.total_tokens * a.groups + 7) / 8 * 8;  // whole XCD rounds
+  const int64_t blocks = (tiles * a.groups + 7) / 8 * 8;  // whole XCD rounds
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((kv_write_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
