@@ -15,7 +15,9 @@ the caches rotate over copies so that the 256 MB last-level cache cannot hold a 
 set.  The roofline figure times the attention call alone: back-to-back calls between two HIP
 events on the launch stream.
 
---only NAME runs just one workload's timed calls (for counter runs under rocprofv3).
+--only NAME runs just one workload's timed calls (for counter runs under rocprofv3);
+chunked_prefill_bf16_write times the six chunk writes of the prefill stack instead of its
+attention calls.
 """
 from __future__ import annotations
 
@@ -646,11 +648,11 @@ def run_tiny(dev, with_oracle):
 def run_only(name, dev, args):
     """Only the timed calls of one workload (for counter runs): set-up, then `steps` attention
     calls (and, for the prefill stack, writes)."""
-    if name == "chunked_prefill_bf16":
+    if name in ("chunked_prefill_bf16", "chunked_prefill_bf16_write"):
         pf = PrefillBench(dev)
-        for li in range(len(pf.layers)):
-            time_calls(lambda i, li=li: pf.attend(li), 1, args.steps, 1)
-        return {"only": name}
+        fn = pf.write if name.endswith("_write") else pf.attend
+        ms = [time_calls(lambda i, li=li: fn(li), 1, args.steps, 1) for li in range(len(pf.layers))]
+        return {"only": name, "per_layer_ms": [round(x, 4) for x in ms]}
     exact = name.endswith("_exact")
     db = DecodeBench(name[:-6] if exact else name, 2, dev, exact=exact)
     ms = time_calls(db.attend, len(db.kcs), args.steps, args.warmup)
