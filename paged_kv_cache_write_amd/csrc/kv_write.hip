@@ -6,15 +6,16 @@
 // lanes cover a row, and one wave instruction covers TT = 64 / R rows (4 at head size 256 in
 // bf16): a row group.
 //
-// A workgroup (4 waves) owns a tile of TT consecutive new tokens and a group of head slots
-// (q heads, then k heads, then v heads).  Row group g of the workgroup is one head slot for the
-// TT tokens of the tile, the tokens side by side.  So when the tokens are consecutive
-// positions of one sequence (a chunk), the lanes holding unit u of the TT rows write TT
-// consecutive rows of the same page column: the value elements of a transposed V page
-// ([d][16 rows]) merge into one request of 2 TT bytes instead of TT requests of 2 bytes, and
-// the K units ([unit column][16 rows]) into 16 TT contiguous bytes.  Large batches give a
-// workgroup all slots of its tile; small ones (a decode step) split them over several
-// workgroups so that the launch still fills the chip.
+// For chunks (on average 16 or more new tokens per sequence) a workgroup (4 waves) owns a tile
+// of TT consecutive new tokens and a group of head slots (q heads, then k heads, then v heads).
+// Row group g of the workgroup is one head slot for the TT tokens of the tile, the tokens side
+// by side.  The tokens are then consecutive positions of one sequence, so the lanes holding
+// unit u of the TT rows write TT consecutive rows of the same page column: the value elements
+// of a transposed V page ([d][16 rows]) merge into one request of 2 TT bytes instead of TT
+// requests of 2 bytes, and the K units ([unit column][16 rows]) into 16 TT contiguous bytes.
+// Otherwise (a decode step) a workgroup owns one token and a row group holds TT of its head
+// slots.  Large batches give a workgroup all slots of its item; small ones split them over
+// several workgroups so that the launch still fills the chip.
 //
 // Order of work in a workgroup: each wave issues the loads of its first row groups before
 // anything else (they depend only on the tile), then every row's R lanes find the sequence
@@ -140,6 +141,15 @@ __device__ __forceinline__ int find_owner(const KvWriteArgs& a, int64_t tok, int
   int lo = 0, hi = tok < a.total_tokens ? a.batch : 0;  // the owner lies in [lo, hi)
   int found = -1;
   int64_t pos = 0;
+  // first guess, checked together with the first round's probes: sequence tok * batch / total
+  // (exact for one new token per sequence, a decode step, and for equal chunks)
+  int gc0 = 0, gc1 = 0, glen = 0, guess = 0;
+  if (hi > 0) {
+    guess = (int)(tok * a.batch / a.total_tokens);
+    gc0 = a.cu[guess];
+    gc1 = a.cu[guess + 1];
+    glen = a.ctx[guess];
+  }
   // rounds: about log_R(batch), the same for every row (the bound depends on batch only)
   for (;;) {
     const bool active = found < 0 && hi - lo >= 1;
@@ -155,6 +165,13 @@ __device__ __forceinline__ int find_owner(const KvWriteArgs& a, int64_t tok, int
         len = a.ctx[i];
       }
     }
+    if (active && gc0 <= tok && tok < gc1) {  // the guess owns tok (its row is done)
+      found = guess;
+      pos = (int64_t)glen - (gc1 - gc0) + (tok - gc0);
+      gc0 = gc1 = 0;  // checked once
+      continue;
+    }
+    gc0 = gc1 = 0;
     const uint64_t all = __ballot(probe && c0 <= tok);
     const uint64_t mine = R == 64 ? all : (all >> base) & ((1ull << (R & 63)) - 1);
     const int last = mine ? 63 - __builtin_clzll(mine) : 0;
@@ -181,20 +198,24 @@ __device__ __forceinline__ int find_owner(const KvWriteArgs& a, int64_t tok, int
   return found;
 }
 
-template <typename T, int D>
+// TILED: a work item is a tile of TT tokens and a row group one head slot of those tokens
+// (chunks); otherwise a work item is one token and a row group TT head slots of it (decode
+// steps, where the tokens of a tile would belong to different sequences and gain nothing).
+template <typename T, int D, bool TILED>
 __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
   using G = Geo<T, D>;
   using C = Calc<T>;
   constexpr int E = G::E, H = G::H, R = G::R, TT = G::TT;
+  constexpr int NT = TILED ? TT : 1;  // tokens per work item
   constexpr int U = kRowGroupsInFlight;
   // rotation tables, laid out [token][element e][unit u] (frequency k = uE + e) so that the
   // lanes of a row read consecutive doubles; each token's table is padded by 16 doubles so
   // that the tokens of a row group fall on different halves of the banks
   constexpr int TS = H + 16;
-  __shared__ double cos_t[TT * TS], sin_t[TT * TS];
+  __shared__ double cos_t[NT * TS], sin_t[NT * TS];
   __shared__ float w_lds[3][D];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int rr = lane / R, ul = lane % R;  // token of the tile (row of the group), unit
+  const int rr = lane / R, ul = lane % R;  // row of the group, unit of the half-row
   // Workgroup ids are dealt to the 8 XCDs round robin; remap them so that each XCD takes a
   // contiguous range of (tile, slot group) items: neighbouring tiles share cache pages, so
   // their partial-line stores meet in one L2 and leave it as whole lines.  The grid is a
@@ -203,15 +224,16 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
   const int64_t item = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   const int64_t tile = item / a.groups;
   const int group = (int)(item - tile * a.groups);
-  const int64_t tok0 = tile * TT;
+  const int64_t tok0 = tile * NT;
   if (tok0 >= a.total_tokens) return;
-  const int64_t tok = tok0 + rr;  // this lane's token
+  const int64_t tok = tok0 + (TILED ? rr : 0);  // this lane's token
   const bool tok_ok = tok < a.total_tokens;
   const int s0 = group * a.slots_per_wg;
   const int s1 = s0 + a.slots_per_wg < a.nslots ? s0 + a.slots_per_wg : a.nslots;
-  const int ngroups = s1 - s0;  // row groups (head slots) of this workgroup
+  const int ngroups = TILED ? s1 - s0 : (s1 - s0 + TT - 1) / TT;  // row groups of the item
 
-  // this lane's row in row group g: head slot s0 + g of token tok
+  // this lane's row in row group g: head slot s0 + g of token tok (TILED), or head slot
+  // s0 + TT g + rr of the item's token
   struct Row {
     bool valid;
     int kind, h;  // kind 0 = q, 1 = k, 2 = v
@@ -219,8 +241,8 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
     u32x4_t u1, u2;
   };
   auto locate = [&](int g, Row& r) {
-    const int slot = s0 + g;
-    r.valid = g < ngroups && tok_ok;
+    const int slot = TILED ? s0 + g : s0 + TT * g + rr;
+    r.valid = g < ngroups && tok_ok && slot < s1;
     const int sq = a.has_q ? a.Hq : 0;
     if (slot < sq) { r.kind = 0; r.h = slot; }
     else if (slot - sq < a.Hkv) { r.kind = 1; r.h = slot - sq; }
@@ -255,7 +277,8 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
 
   // the owning sequence, position and block of this lane's token
   int64_t t = 0;
-  const int b = find_owner<R>(a, tok, t);
+  // (untiled, every lane holds the same token: one 64-ary search)
+  const int b = find_owner<TILED ? R : kWave>(a, tok, t);
   const bool pos_ok = b >= 0 && t >= 0;  // the row has a position (q needs nothing more)
   if (tok_ok && b < 0) debug_flag(kDbgOwner);   // cu_seqlens inconsistent: the row is skipped
   if (b >= 0 && t < 0) debug_flag(kDbgLength);  // n_b > L_b: skipped
@@ -278,7 +301,7 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
   // held by lane R j of every wave (every wave computes the same owners).
   const bool rope = a.theta > 0.0;
   if (rope) {
-    for (int q = threadIdx.x; q < TT * H; q += 256) {
+    for (int q = threadIdx.x; q < NT * H; q += 256) {
       const int j = q / H, k = q - j * H;
       const int64_t tj = __shfl(t, R * j, kWave);
       double sn = 0.0, cs = 1.0;
@@ -325,8 +348,8 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
       else inv = 1.0 / sqrt(ss / D + a.eps);
     }
     const float* w = w_lds[r.kind];  // all ones when the tensor has no weight
-    const double* cj = cos_t + rr * TS + ul;  // element e at cj[e R]
-    const double* sj = sin_t + rr * TS + ul;
+    const double* cj = cos_t + (TILED ? rr : 0) * TS + ul;  // element e at cj[e R]
+    const double* sj = sin_t + (TILED ? rr : 0) * TS + ul;
     if constexpr (sizeof(T) == 2) {
       if (rot) {
 #pragma unroll
@@ -398,23 +421,34 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
   }
 }
 
+template <typename T, int D, bool TILED>
+hipError_t launch_tiled(KvWriteArgs a, hipStream_t s) {
+  using G = Geo<T, D>;
+  constexpr int NT = TILED ? G::TT : 1;        // tokens per work item
+  constexpr int SPG = TILED ? 1 : G::TT;       // head slots per row group
+  // Slots per workgroup: all of an item's when there are enough items to fill the chip (about
+  // 2048 workgroups of 4 waves), otherwise down to one row group per wave.
+  const int64_t items = ((int64_t)a.total_tokens + NT - 1) / NT;
+  const int64_t rg_per_item = (a.nslots + SPG - 1) / SPG;
+  const int64_t rgs = items * rg_per_item;
+  int64_t per_wave = (rgs + 4 * 2048 - 1) / (4 * 2048);
+  const int64_t max_per_wave = (rg_per_item + 3) / 4;
+  per_wave = per_wave < 1 ? 1 : (per_wave > max_per_wave ? max_per_wave : per_wave);
+  a.slots_per_wg = (int)(4 * per_wave * SPG);
+  a.groups = (a.nslots + a.slots_per_wg - 1) / a.slots_per_wg;
+  const int64_t blocks = (items * a.groups + 7) / 8 * 8;  // whole XCD rounds
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((kv_write_kernel<T, D, TILED>), dim3((unsigned)blocks), dim3(256), 0, s,
+                     a);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_t(KvWriteArgs a, hipStream_t s) {
-  using G = Geo<T, D>;
   if (a.total_tokens == 0 || a.nslots == 0) return hipSuccess;
-  // Slots per workgroup: all of a tile's when there are enough tiles to fill the chip (about
-  // 2048 workgroups of 4 waves), otherwise down to one row group per wave.
-  const int64_t tiles = ((int64_t)a.total_tokens + G::TT - 1) / G::TT;
-  const int64_t rgs = tiles * a.nslots;
-  int64_t per_wave = (rgs + 4 * 2048 - 1) / (4 * 2048);
-  const int64_t max_per_wave = (a.nslots + 3) / 4;
-  per_wave = per_wave < 1 ? 1 : (per_wave > max_per_wave ? max_per_wave : per_wave);
-  a.slots_per_wg = (int)(4 * per_wave);
-  a.groups = (a.nslots + a.slots_per_wg - 1) / a.slots_per_wg;
-  const int64_t blocks = (tiles * a.groups + 7) / 8 * 8;  // whole XCD rounds
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((kv_write_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-  return hipGetLastError();
+  // token tiles pay off for chunks (on average 16 or more new tokens per sequence)
+  return (int64_t)a.total_tokens >= (int64_t)kPage * a.batch ? launch_tiled<T, D, true>(a, s)
+                                                              : launch_tiled<T, D, false>(a, s);
 }
 
 }  // namespace
