@@ -45,7 +45,9 @@ def build(force: bool = False) -> str:
 def _load():
     global _lib
     if _lib is None:
-        lib = ctypes.CDLL(build())
+        # the sanitizer run of the CPU test-suite points this at an instrumented build
+        path = os.environ.get("GA_ORACLE_LIB") or build()
+        lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i32, i64, dbl = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
         lib.ref_num_threads.restype = ctypes.c_int
