@@ -48,14 +48,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// Two fp32 -> packed bf16x2 (lo in bits 0..15), round to nearest even.
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
-}
-
-// Two fp32 -> bf16x2 with the hardware conversion (round to nearest even).
+// Two fp32 -> bf16x2 with the hardware conversion (round to nearest even; NaN stays NaN).
 __device__ __forceinline__ bf16x2_t cvt_bf16x2(float lo, float hi) {
   return __builtin_convertvector(float2_t{lo, hi}, bf16x2_t);
+}
+
+// The same conversion, packed (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, cvt_bf16x2(lo, hi));
 }
 
 // acc + w.x + w.y in fp32 (one dot-product instruction).

@@ -58,27 +58,34 @@
 namespace ga {
 namespace {
 
-constexpr int kWaves = 8;             // two waves per SIMD, 256 registers each
 constexpr int kPF = 3;                // operand fragment reads in flight ahead of their products
 constexpr int kRun = 4;               // consecutive row tiles of a group given to one XCD
 
+// Waves per workgroup, two per SIMD on a CU either way (256 registers each): 8 in one
+// workgroup per CU at head size 512 and for the exact K=V form, 4 in each of two workgroups per
+// CU elsewhere (LDS rings of 64 KiB).  The waves of two workgroups are not held in step by each
+// other's barriers, so one workgroup's softmax and its prologue and epilogue run beside the
+// other's matrix-core work.
+template <int D, bool EXACT>
+constexpr int waves_for() { return D <= 256 && !EXACT ? 4 : 8; }
+
 // MFMA column blocks per wave: 2 (32 rows) up to head size 256, 1 (16 rows) at 512, where
 // 32 rows of Q^T (128 registers) plus O^T (256) would not fit a wave's 256 registers.
-template <int D>
+template <int D, int NW>
 struct Rows {
   static constexpr int kR = D == 512 ? 1 : 2;
   static constexpr int kPerWave = 16 * kR;
-  static constexpr int kPerWg = kWaves * kPerWave;
+  static constexpr int kPerWg = NW * kPerWave;
 };
 
-// LDS: a ring of SK K tiles and a ring of SV V^T tiles (K=V: the K ring only) in 128 KiB
-// (measured: a 160 KiB allocation with a deeper K ring at head size 512 runs slower).
+// LDS: a ring of SK K tiles and a ring of SV V^T tiles (K=V: the K ring only) in 16 KiB per
+// wave (measured: a 160 KiB allocation with a deeper K ring at head size 512 runs slower).
 // Iteration it reads K(it) and V(it).
-template <int D, bool KEQV>
+template <int D, bool KEQV, int NW>
 struct TileLds {
   static constexpr int kPageBytes = kPage * D * 2;  // one page of K (or V^T)
   static constexpr int kTile = 2 * kPageBytes;      // one 32-key tile of K (or of V^T)
-  static constexpr int kBudget = 128 * 1024;
+  static constexpr int kBudget = NW * 16 * 1024;
   static constexpr int kMaxStages = 4;
   static constexpr int kFit = kBudget / kTile;      // tiles that fit
   static constexpr int SK = KEQV ? (kFit < kMaxStages ? kFit : kMaxStages)
@@ -88,8 +95,8 @@ struct TileLds {
   static constexpr int kVRing = SK * kTile;
   static constexpr int kBytes = (SK + SV) * kTile;
   static constexpr int kChunks = kTile / 1024;          // 1 KiB copies per tile
-  static constexpr int kPerWave = kChunks / kWaves;     // copies per wave per tile
-  static_assert(kChunks % kWaves == 0, "tile copies split evenly over the waves");
+  static constexpr int kPerWave = kChunks / NW;         // copies per wave per tile
+  static_assert(kChunks % NW == 0, "tile copies split evenly over the waves");
   static_assert(SK >= 2 && SK <= kMaxStages && (KEQV ? SK >= 3 : (SV >= 2 && SV <= SK)),
                 "ring depths");
   static_assert(kBytes <= kBudget, "LDS budget");
@@ -103,16 +110,16 @@ struct TileLds {
 };
 
 // Copy i (0 .. kPerWave-1) of this wave for one tile of K (V=false) or of V^T (V=true) into
-// `lds_off`: 1 KiB chunk q = wave + kWaves * i of the tile, from a wave-uniform base plus the
+// `lds_off`: 1 KiB chunk q = wave + NW * i of the tile, from a wave-uniform base plus the
 // per-lane offset 16 lane.  Both page kinds are copied as they are stored (K pages already hold
 // the LDS arrangement: k_page_elem), so every copy reads one contiguous 1 KiB run.
-template <int D, bool KEQV, bool V>
+template <int D, bool KEQV, bool V, int NW>
 __device__ __forceinline__ void issue_chunk(const AttnArgs& a, uint32_t lds_off, int g,
                                             int64_t blkA, int64_t blkB, int wave, int i,
                                             uint32_t vlane) {
-  using T = TileLds<D, KEQV>;
+  using T = TileLds<D, KEQV, NW>;
   constexpr int kChunksPerPage = T::kPageBytes / 1024;
-  const int q = wave + kWaves * i;  // 1 KiB chunk of the tile (wave-uniform)
+  const int q = wave + NW * i;  // 1 KiB chunk of the tile (wave-uniform)
   const int page = q / kChunksPerPage, qq = q - page * kChunksPerPage;
   const int64_t blk = page ? blkB : blkA;
   const int64_t page_bytes = ((blk * a.Hkv + g) * kPage * D) * 2;
@@ -122,12 +129,12 @@ __device__ __forceinline__ void issue_chunk(const AttnArgs& a, uint32_t lds_off,
 
 // Zero, in one staged tile, the values of key slots nvalid .. 31 (keys past the context):
 // the V^T pages (or, K=V, the K pages, which then serve as values).  All threads take part.
-template <int D, bool KEQV>
+template <int D, bool KEQV, int NW>
 __device__ __forceinline__ void zero_tail_values(unsigned char* tile, int nvalid) {
-  using T = TileLds<D, KEQV>;
+  using T = TileLds<D, KEQV, NW>;
   if constexpr (!KEQV) {
     // V^T page [D rows][16 keys]: one row (32 bytes) of one page per step
-    for (int q = threadIdx.x; q < 2 * D; q += 64 * kWaves) {
+    for (int q = threadIdx.x; q < 2 * D; q += 64 * NW) {
       const int page = q / D, d = q - page * D;
       unsigned char* row = tile + page * T::kPageBytes + d * 32;
 #pragma unroll
@@ -137,7 +144,7 @@ __device__ __forceinline__ void zero_tail_values(unsigned char* tile, int nvalid
     }
   } else {
     // chunk-major K page: 16-byte unit (row r, chunk x) at 256 x + 16 k_slot(r, x, page)
-    for (int q = threadIdx.x; q < 2 * kPage * (D / 8); q += 64 * kWaves) {
+    for (int q = threadIdx.x; q < 2 * kPage * (D / 8); q += 64 * NW) {
       const int page = q / (kPage * (D / 8)), u = q - page * (kPage * (D / 8));
       const int x = u >> 4, r = u & 15;
       if (page * kPage + r >= nvalid)
@@ -169,11 +176,12 @@ constexpr int rope_chunk_of() {
 // pair per thread) into a separate LDS buffer that the QK^T fragment reads of those chunks
 // use; the values are still read from the unrotated tile.
 template <int D, int SM, bool KEQV, bool EXACT>
-__global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs a, int runs_per_bg,
-                                                                     int n_groups) {
-  using T = TileLds<D, KEQV>;
-  constexpr int NC = D / 32, ND = D / 16, R = Rows<D>::kR, SK = T::SK, SV = T::SV;
-  constexpr int kRowsPerWave = Rows<D>::kPerWave, kRowsPerWg = Rows<D>::kPerWg;
+__global__ __launch_bounds__((64 * waves_for<D, EXACT>()), (8 / waves_for<D, EXACT>())) void
+prefill_tiled_kernel(AttnArgs a, int runs_per_bg, int n_groups) {
+  constexpr int NW = waves_for<D, EXACT>();
+  using T = TileLds<D, KEQV, NW>;
+  constexpr int NC = D / 32, ND = D / 16, R = Rows<D, NW>::kR, SK = T::SK, SV = T::SV;
+  constexpr int kRowsPerWave = Rows<D, NW>::kPerWave, kRowsPerWg = Rows<D, NW>::kPerWg;
   extern __shared__ __align__(16) unsigned char smem[];
   const uint32_t smem_off =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
@@ -224,7 +232,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
   int lo_c[R];
   uint32_t span_c[R];
   bool ok_c[R];
-  bf16x8_t qf[R][NC];
+  int64_t q_off[R];  // element offset of this lane's Q row
+  bf16x8_t qf[R][NC];  // loaded after the first tile copies are issued
 #pragma unroll
   for (int rb = 0; rb < R; ++rb) {
     const int rr = 16 * rb + c16;
@@ -235,18 +244,17 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
     const int lo = W > 0 ? (t - W + 1 > 0 ? t - W + 1 : 0) : 0;
     lo_c[rb] = ok_c[rb] ? lo : (1 << 30);
     span_c[rb] = ok_c[rb] ? (uint32_t)(t - lo) : 0u;
-    load_q<D>(qf[rb], a.q + ((int64_t)(q0 + i) * a.Hq + g * G + hh) * D, ok_c[rb]);
+    q_off[rb] = ((int64_t)(q0 + i) * a.Hq + g * G + hh) * D;
   }
-  // Complete the Q loads here: left to the compiler, their wait would sit at the first use,
-  // inside the tile loop, and drain the in-flight tile copies on every iteration.
-  wait_vmcnt<0>();
   // wave-uniform bounds: intersection [lo_max, hi_min] of the rows' key ranges (tiles inside it
-  // need no mask)
+  // need no mask) and their union [lo_min, hi_max] (tiles outside it are skipped)
   const bool wave_active = wrows > 0;
   const int t_first_w = past + (wave_active ? wrow0 : row0) / G;
   const int t_last_w = past + (wave_active ? wrow0 + wrows - 1 : row0) / G;
   const int lo_max = W > 0 ? (t_last_w - W + 1 > 0 ? t_last_w - W + 1 : 0) : 0;
   const int hi_min = t_first_w;
+  const int lo_min = W > 0 ? (t_first_w - W + 1 > 0 ? t_first_w - W + 1 : 0) : 0;
+  const int hi_max = wave_active ? t_last_w : -1;
 
   float m_ref[R], l_run[R];
   float4_t o[R][ND];
@@ -326,12 +334,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
   constexpr int kWait = (S / TB - 2) * TB * kPerTile;  // copies of later iterations in flight
   const uint32_t vlane = 16u * lane;
   auto k_chunk = [&](int t, const TileIds& ids, int i) {
-    issue_chunk<D, KEQV, false>(a, smem_off + T::kKRing + (t % S) * T::kTile, g, ids.a, ids.b,
+    issue_chunk<D, KEQV, false, NW>(a, smem_off + T::kKRing + (t % S) * T::kTile, g, ids.a, ids.b,
                                 wave, i, vlane);
   };
   auto v_chunk = [&](int t, const TileIds& ids, int i) {
     if constexpr (!KEQV)
-      issue_chunk<D, KEQV, true>(a, smem_off + T::kVRing + (t % S) * T::kTile, g, ids.a,
+      issue_chunk<D, KEQV, true, NW>(a, smem_off + T::kVRing + (t % S) * T::kTile, g, ids.a,
                                  ids.b, wave, i, vlane);
   };
   auto issue_tile = [&](int t, const TileIds& ids) {
@@ -496,14 +504,21 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
     }
   };
 
-  // prologue: tiles 0 .. S - TB - 1
+  // prologue: tiles 0 .. S - TB - 1, then the Q fragments, so that the latencies of both
+  // overlap.  All of them are complete before the loop: left to the compiler, the wait for the
+  // Q loads would sit at their first use, inside the tile loop, and drain the in-flight tile
+  // copies on every iteration.
   for (int t = 0; t < S - TB; ++t) issue_tile(t, ids_of(t));
+#pragma unroll
+  for (int rb = 0; rb < R; ++rb) load_q<D>(qf[rb], a.q + q_off[rb], ok_c[rb]);
+  wait_vmcnt<0>();
   TileIds cids[TB];
 #pragma unroll
   for (int u = 0; u < TB; ++u) cids[u] = ids_of(S - TB + u);
 
-  const int nsuper = (np + TB - 1) / TB;
-  for (int jj = 0; jj < nsuper; ++jj) {
+  // Iteration jj starts with the same steps in every wave: the wait for its tiles, the barrier
+  // and the cooperative fix-ups of the staged tiles
+  auto iteration_begin = [&](int jj) {
     // this iteration's tiles have landed once at most the copies of later iterations remain
     wait_vmcnt<kWait>();
     __syncthreads();
@@ -512,7 +527,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
       if (tl >= TB * jj && tl < TB * jj + TB && (kt0 + tl) * kTileKeys + kTileKeys > L) {
         // slots of keys >= L may hold anything, NaN included, and a zero weight does not
         // cancel a NaN value: zero the values of those keys once, in LDS
-        zero_tail_values<D, KEQV>(smem + (KEQV ? T::kKRing : T::kVRing) + (tl % S) * T::kTile,
+        zero_tail_values<D, KEQV, NW>(smem + (KEQV ? T::kKRing : T::kVRing) + (tl % S) * T::kTile,
                                   L - (kt0 + tl) * kTileKeys);
         __syncthreads();
       }
@@ -543,17 +558,53 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
       }
       __syncthreads();
     }
-    // Every wave runs every tile of the workgroup's range: a tile outside a wave's band is
-    // masked whole (its weights are exactly 0) and costs a little matrix-core time, where a
-    // branch around the work would split the copy schedule spread over it.
+  };
+  // ... and ends by fetching the ids of the tiles the next one copies (here, not at the
+  // barrier, where every wave of the workgroup would wait for them at the same moment)
+  auto iteration_end = [&](int jj) {
+#pragma unroll
+    for (int u = 0; u < TB; ++u) cids[u] = ids_of(TB * (jj + 1) + S - TB + u);
+  };
+  // A wave computes only the iterations whose tiles hold a key that one of its rows sees (a
+  // sliding window's band is narrower than the workgroup's key range by the workgroup's span of
+  // positions, and a wave without rows sees nothing); in the others it only takes its share of
+  // the copies.  Three loops rather than a branch per iteration keep the register allocation of
+  // the computing loop as it is without them.
+  const int nsuper = (np + TB - 1) / TB;
+  const int own_lo = lo_min / kTileKeys - kt0, own_hi = hi_max / kTileKeys - kt0;
+  const int jj_lo = hi_max < 0 ? nsuper : (own_lo > 0 ? own_lo / TB : 0);
+  const int jj_hi = hi_max < 0 ? nsuper : (own_hi / TB + 1 < nsuper ? own_hi / TB + 1 : nsuper);
+  auto copies_only = [&](int jj) {
+    constexpr int Q = TB * T::kPerWave;
+    const int ct = TB * jj + S - TB;
+    sfor<Q>([&](auto qc) {
+      constexpr int q = decltype(qc)::value;
+      k_chunk(ct + q / T::kPerWave, cids[q / T::kPerWave], q % T::kPerWave);
+    });
+    sfor<Q>([&](auto qc) {
+      constexpr int q = decltype(qc)::value;
+      v_chunk(ct + q / T::kPerWave, cids[q / T::kPerWave], q % T::kPerWave);
+    });
+  };
+  for (int jj = 0; jj < jj_lo; ++jj) {
+    iteration_begin(jj);
+    copies_only(jj);
+    iteration_end(jj);
+  }
+  for (int jj = jj_lo; jj < jj_hi; ++jj) {
+    iteration_begin(jj);
+    // a tile of the iteration outside the wave's band is masked whole (its weights are
+    // exactly 0)
     process_tile(TB * jj, std::integral_constant<int, TB>{}, TB * jj + S - TB, cids);
     if constexpr (TB == 2) {
       if (TB * jj + 1 < np) process_tile(TB * jj + 1, std::integral_constant<int, 0>{}, 0, cids);
     }
-    // the next iteration's tile ids, fetched here (not at the barrier, where every wave of
-    // the workgroup would wait for them at the same moment)
-#pragma unroll
-    for (int u = 0; u < TB; ++u) cids[u] = ids_of(TB * (jj + 1) + S - TB + u);
+    iteration_end(jj);
+  }
+  for (int jj = jj_hi; jj < nsuper; ++jj) {
+    iteration_begin(jj);
+    copies_only(jj);
+    iteration_end(jj);
   }
   wait_vmcnt<0>();  // no copy may land in LDS after the workgroup has left it
 
@@ -589,9 +640,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_tiled_kernel(AttnArgs 
 
 template <int D, int SM, bool KEQV, bool EXACT>
 hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
-  using T = TileLds<D, KEQV>;
+  constexpr int NW = waves_for<D, EXACT>();
+  using T = TileLds<D, KEQV, NW>;
   constexpr int kLds = T::kBytes + (EXACT ? T::kRopeBytes : 0);
-  constexpr int kRowsPerWg = Rows<D>::kPerWg;
+  constexpr int kRowsPerWg = Rows<D, NW>::kPerWg;
   const int64_t tiles_per_bg = ((int64_t)a.max_q_len * a.G + kRowsPerWg - 1) / kRowsPerWg;
   const int64_t runs_per_bg = (tiles_per_bg + kRun - 1) / kRun;
   const int64_t n_groups = (int64_t)a.Hkv * a.batch;
@@ -605,7 +657,7 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((prefill_tiled_kernel<D, SM, KEQV, EXACT>), dim3((unsigned)grid),
-                     dim3(64 * kWaves),
+                     dim3(64 * NW),
                      kLds, s, a, (int)runs_per_bg, (int)n_groups);
   return hipGetLastError();
 }
