@@ -17,6 +17,13 @@
 // slots.  Large batches give a workgroup all slots of its item; small ones split them over
 // several workgroups so that the launch still fills the chip.
 //
+// Values of chunks in bf16 take a pass of their own (kv_write_v_kernel): a workgroup owns 16
+// consecutive new tokens and a group of v heads.  Each row is normalised as above, then the
+// workgroup stages the head's [d][16 tokens] block in LDS, and 16 consecutive lanes store one
+// dimension of the 16 tokens, so the tokens of one page row leave as one contiguous run (two
+// when the tile crosses a page).  Measured: a page row written 4 tokens at a time costs about
+// as much as all other stores of the chunk together.
+//
 // Order of work in a workgroup: each wave issues the loads of its first row groups before
 // anything else (they depend only on the tile), then every row's R lanes find the sequence
 // owning the row's token by an R-ary search of cu_seqlens (one round of loads for up to R
@@ -421,6 +428,124 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
   }
 }
 
+constexpr int kVTile = 16;  // tokens per workgroup of the value pass (one page row)
+
+// The value pass of a bf16 chunk write: v rows of tokens tok0 .. tok0 + 15 for heads
+// h0 .. h1 - 1 (RMSNorm with w_v, no rotation), stored into the transposed V pages.
+template <int D>
+__global__ __launch_bounds__(256) void kv_write_v_kernel(KvWriteArgs a) {
+  using T = uint16_t;
+  using G = Geo<T, D>;
+  constexpr int E = G::E, H = G::H, R = G::R, TT = G::TT;
+  constexpr int NQ = kVTile / TT;      // row groups (TT tokens each) of the tile
+  constexpr int QW = (NQ + 3) / 4;     // row groups per wave
+  constexpr int SD = kVTile + 1;       // staged dimension row, padded (odd): the 16 row lanes
+                                       // writing one element index fall on distinct banks
+  static_assert(kVTile % TT == 0, "tile of whole row groups");
+  __shared__ uint16_t stage[D * SD];
+  __shared__ float w_lds[D];
+  __shared__ int64_t tok_base[kVTile];  // element offset of (block, slot) of each token, or -1
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rr = lane / R, ul = lane % R;
+  // XCD-contiguous ranges of (tile, head group) items, as in kv_write_kernel
+  const int64_t per_xcd = gridDim.x / 8;
+  const int64_t item = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  const int64_t tile = item / a.groups;
+  const int group = (int)(item - tile * a.groups);
+  const int64_t tok0 = tile * kVTile;
+  if (tok0 >= a.total_tokens) return;
+  const int h0 = group * a.slots_per_wg;
+  const int h1 = h0 + a.slots_per_wg < a.Hkv ? h0 + a.slots_per_wg : a.Hkv;
+
+  // this wave's rows: row group qg = wave + 4 i holds tokens tok0 + TT qg .. + TT - 1
+  bool valid[QW];
+  int64_t tokr[QW];
+  u32x4_t u1[QW], u2[QW];
+  auto load = [&](int h) {
+#pragma unroll
+    for (int i = 0; i < QW; ++i)
+      if (valid[i]) {
+        const T* src = (const T*)a.v + (tokr[i] * a.Hkv + h) * (int64_t)D;
+        u1[i] = *(const u32x4_t*)(src + ul * E);
+        u2[i] = *(const u32x4_t*)(src + H + ul * E);
+      }
+  };
+#pragma unroll
+  for (int i = 0; i < QW; ++i) {
+    const int qg = wave + 4 * i;
+    tokr[i] = tok0 + TT * qg + rr;
+    valid[i] = qg < NQ && tokr[i] < a.total_tokens;
+  }
+  load(h0);
+  if (threadIdx.x < D) w_lds[threadIdx.x] = a.wv ? a.wv[threadIdx.x] : 1.f;
+  if (D > 256 && threadIdx.x + 256 < D) w_lds[threadIdx.x + 256] = a.wv ? a.wv[threadIdx.x + 256] : 1.f;
+  // owner, position and cache slot of each row's token (every lane of the wave searches)
+#pragma unroll
+  for (int i = 0; i < QW; ++i) {
+    int64_t t = 0;
+    const int b = find_owner<R>(a, valid[i] ? tokr[i] : (int64_t)a.total_tokens, t);
+    int64_t base = -1;
+    if (valid[i]) {
+      if (b < 0) debug_flag(kDbgOwner);
+      if (b >= 0 && t < 0) debug_flag(kDbgLength);
+      if (b >= 0 && t >= 0) {
+        const int64_t page = t >> 4;
+        if (!a.ring && page >= a.max_blocks) {
+          debug_flag(kDbgBound);
+        } else {
+          const int64_t blk = a.bt[(int64_t)b * a.max_blocks +
+                                   bt_col((int)page, a.max_blocks, a.ring)];
+          if (blk < 0 || blk >= a.num_blocks) debug_flag(kDbgBlockId);
+          else base = blk * a.Hkv * (int64_t)D * kPage + (t & 15);
+        }
+      }
+    }
+    if (valid[i] && ul == 0) tok_base[TT * (wave + 4 * i) + rr] = base;
+    if (!valid[i] && ul == 0 && wave + 4 * i < NQ) tok_base[TT * (wave + 4 * i) + rr] = -1;
+  }
+  __syncthreads();
+  const int sj = threadIdx.x % kVTile;  // the store phase: token sj, dimensions threadIdx.x / 16 + 16 k
+  const int64_t my_base = tok_base[sj];
+
+  for (int h = h0; h < h1; ++h) {
+    // normalise this wave's rows of head h into the staging block
+#pragma unroll
+    for (int i = 0; i < QW; ++i) {
+      if (!valid[i]) continue;  // whole rows: the norm's shuffles stay inside a row
+      float x1[E], x2[E];
+      unpack<T>(u1[i], x1);
+      unpack<T>(u2[i], x2);
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) ss += x1[e] * x1[e] + x2[e] * x2[e];
+#pragma unroll
+      for (int m = R / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, kWave);
+      const float inv = a.wv ? rsqrtf(ss / (float)D + (float)a.eps) : 1.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        x1[e] = x1[e] * w_lds[ul * E + e] * inv;
+        x2[e] = x2[e] * w_lds[H + ul * E + e] * inv;
+      }
+      const u32x4_t o1 = pack<T>(x1), o2 = pack<T>(x2);
+      const int j = TT * (wave + 4 * i) + rr;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        stage[(ul * E + e) * SD + j] = (uint16_t)(o1[e >> 1] >> (16 * (e & 1)));
+        stage[(H + ul * E + e) * SD + j] = (uint16_t)(o2[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+    if (h + 1 < h1) load(h + 1);  // the next head's rows, in flight during the stores
+    __syncthreads();
+    if (my_base >= 0) {
+      T* dst = (T*)a.vc + my_base + (int64_t)h * D * kPage;
+#pragma unroll 4
+      for (int d = threadIdx.x / kVTile; d < D; d += 256 / kVTile)
+        dst[(int64_t)d * kPage] = stage[d * SD + sj];
+    }
+    __syncthreads();
+  }
+}
+
 template <typename T, int D, bool TILED>
 hipError_t launch_tiled(KvWriteArgs a, hipStream_t s) {
   using G = Geo<T, D>;
@@ -443,12 +568,36 @@ hipError_t launch_tiled(KvWriteArgs a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_values(KvWriteArgs a, hipStream_t s) {
+  // heads per workgroup: all of them when the tiles alone fill the chip (about 2048
+  // workgroups), fewer otherwise
+  const int64_t tiles = ((int64_t)a.total_tokens + kVTile - 1) / kVTile;
+  int64_t per_wg = (tiles * a.Hkv + 2047) / 2048;
+  per_wg = per_wg < 1 ? 1 : (per_wg > a.Hkv ? a.Hkv : per_wg);
+  a.slots_per_wg = (int)per_wg;
+  a.groups = (int)((a.Hkv + per_wg - 1) / per_wg);
+  const int64_t blocks = (tiles * a.groups + 7) / 8 * 8;  // whole XCD rounds
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((kv_write_v_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_t(KvWriteArgs a, hipStream_t s) {
   if (a.total_tokens == 0 || a.nslots == 0) return hipSuccess;
   // token tiles pay off for chunks (on average 16 or more new tokens per sequence)
-  return (int64_t)a.total_tokens >= (int64_t)kPage * a.batch ? launch_tiled<T, D, true>(a, s)
-                                                              : launch_tiled<T, D, false>(a, s);
+  if ((int64_t)a.total_tokens < (int64_t)kPage * a.batch) return launch_tiled<T, D, false>(a, s);
+  if constexpr (sizeof(T) == 2) {
+    if (a.has_kv && !a.k_eq_v) {  // values in a pass of their own
+      KvWriteArgs qk = a;
+      qk.nslots -= a.Hkv;
+      hipError_t e = qk.nslots > 0 ? launch_tiled<T, D, true>(qk, s) : hipSuccess;
+      if (e != hipSuccess) return e;
+      return launch_values<D>(a, s);
+    }
+  }
+  return launch_tiled<T, D, true>(a, s);
 }
 
 }  // namespace
