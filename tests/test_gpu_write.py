@@ -74,10 +74,14 @@ def test_rope_at_long_positions():
     assert ulp_distance(wl.to_numpy_bits(qd), qh).max() <= 1
 
 
-def test_only_owned_slots_change():
+@pytest.mark.parametrize("lens,news", [
+    ([40, 9], [7, 9]),  # a decode-sized call (one workgroup per token)
+    # chunks: 16-token tiles that straddle sequences and page boundaries (the value pass)
+    ([40, 70, 33, 5], [37, 50, 20, 5]),
+])
+def test_only_owned_slots_change(lens, news):
     """Pages and rows outside the written slots keep their NaN fill (no stray stores)."""
     spec = wl.LayerSpec("bf16", 4, 2, 256)
-    lens, news = [40, 9], [7, 9]
     pb = wl.paged_batch(lens, news, seed=14)
     case = PagedCase(spec, pb, 14)
     case.write(lens, news, 14)
