@@ -20,8 +20,9 @@
 // the QK^T products, V copies among the P.V products) instead of queueing behind the barrier.
 // Operand fragments are read from LDS kPF fragments ahead of the products that use them: the
 // loops are cut into one chunk per fragment by scheduling fences.  Block
-// ids come through the scalar cache, one load per tile, fetched at the end of the previous
-// iteration.  Only tiles that intersect the band [past + i - W + 1, past + i] of some row of
+// ids are held 64 pages at a time in one register per lane and broadcast with readlane (one
+// vector load per 32 tiles); the next tile's page offsets are formed at the end of the
+// previous iteration.  Only tiles that intersect the band [past + i - W + 1, past + i] of some row of
 // the workgroup are visited, and every wave runs all of them (a tile outside a wave's rows is
 // masked whole); tiles whose every key is visible to every row of a wave skip all masking.
 // Keys past the context (only in the last tile) are zeroed in LDS once, so no value read
@@ -111,20 +112,24 @@ struct TileLds {
 
 // Copy i (0 .. kPerWave-1) of this wave for one tile of K (V=false) or of V^T (V=true) into
 // `lds_off`: 1 KiB chunk q = wave + NW * i of the tile, from a wave-uniform base plus the
-// per-lane offset 16 lane.  Both page kinds are copied as they are stored (K pages already hold
-// the LDS arrangement: k_page_elem), so every copy reads one contiguous 1 KiB run.
+// per-lane offset 16 lane.  offA / offB are the byte offsets of the tile's two pages (the same
+// in the K and the V cache).  Both page kinds are copied as they are stored (K pages already
+// hold the LDS arrangement: k_page_elem), so every copy reads one contiguous 1 KiB run.
 template <int D, bool KEQV, bool V, int NW>
-__device__ __forceinline__ void issue_chunk(const AttnArgs& a, uint32_t lds_off, int g,
-                                            int64_t blkA, int64_t blkB, int wave, int i,
-                                            uint32_t vlane) {
+__device__ __forceinline__ void issue_chunk(const AttnArgs& a, uint32_t lds_off, int64_t offA,
+                                            int64_t offB, int wave, int i, uint32_t vlane) {
   using T = TileLds<D, KEQV, NW>;
   constexpr int kChunksPerPage = T::kPageBytes / 1024;
   const int q = wave + NW * i;  // 1 KiB chunk of the tile (wave-uniform)
-  const int page = q / kChunksPerPage, qq = q - page * kChunksPerPage;
-  const int64_t blk = page ? blkB : blkA;
-  const int64_t page_bytes = ((blk * a.Hkv + g) * kPage * D) * 2;
+  // the page of chunk q: known at compile time when the waves divide a page's chunks
+  // (wave < NW), otherwise a scalar select
+  int page;
+  if constexpr (kChunksPerPage % NW == 0) page = NW * i / kChunksPerPage;
+  else page = q / kChunksPerPage;
+  const int qq = q - page * kChunksPerPage;
+  const int64_t off = page ? offB : offA;
   const unsigned char* base = (const unsigned char*)(V ? (const void*)a.vc : (const void*)a.kc);
-  lds_copy16_sv(base + page_bytes + 1024 * qq, vlane, lds_off + q * 1024);
+  lds_copy16_sv(base + off + 1024 * qq, vlane, lds_off + q * 1024);
 }
 
 // Zero, in one staged tile, the values of key slots nvalid .. 31 (keys past the context):
@@ -295,26 +300,31 @@ prefill_tiled_kernel(AttnArgs a, int runs_per_bg, int n_groups) {
   // g - 1 + S into the stages that iteration g - 1 has just released; iteration it reads
   // tile it.
   const int np = ntiles;
-  // Block ids of a tile's two pages (wave-uniform, through the scalar cache).
+  // Byte offsets in the caches of a tile's two pages.  The block ids of the workgroup's pages
+  // are held 64 at a time, lane l holding that of page pw0 + l (clamped; on a ring table each
+  // page's own column), and broadcast with readlane.  A tile's second page lying past the
+  // context aliases its first (its keys are masked and its values zeroed), so nothing past the
+  // sequence's last page is read.  A window is loaded every 32 tiles.
   struct TileIds { int64_t a, b; };
+  int pw0 = -64;     // first page of the window (even; wave-uniform)
+  int win_bid = 0;   // this lane's block id in the window
+  constexpr int64_t kPageBytesG = (int64_t)kPage * D * 2;
   auto ids_of = [&](int tile) -> TileIds {
     TileIds r{0, 0};
     if (tile < 0 || tile >= ntiles) return r;
     const int page = 2 * (kt0 + tile);  // <= last_page for every tile of the range
-    if (page + 1 <= last_page && !a.ring) {
-      const int2 v = scalar_load2(a.bt + bt_row + page);
-      r.a = clamp_blk(v.x, a.num_blocks);
-      r.b = clamp_blk(v.y, a.num_blocks);
-    } else if (page + 1 <= last_page) {  // ring row: the two columns need not be adjacent
-      r.a = clamp_blk(scalar_load1(a.bt + bt_row + bt_col(page, a.max_blocks, 1)), a.num_blocks);
-      r.b = clamp_blk(scalar_load1(a.bt + bt_row + bt_col(page + 1, a.max_blocks, 1)),
-                      a.num_blocks);
-    } else {
-      // the second page lies past the context: alias the first (its keys are masked and its
-      // values zeroed) and read nothing past the sequence's last page
-      r.a = r.b = clamp_blk(scalar_load1(a.bt + bt_row + bt_col(page, a.max_blocks, a.ring)),
-                            a.num_blocks);
+    if (page < pw0 || page - pw0 >= kWave) {
+      // pages past the context take the last page's id: the only one read is the second page
+      // of the last tile when last_page is even, which aliases the first
+      pw0 = page;
+      const int q = page + lane < last_page ? page + lane : last_page;
+      win_bid = (int)clamp_blk(a.bt[bt_row + bt_col(q, a.max_blocks, a.ring)], a.num_blocks);
     }
+    const int i = page - pw0;
+    const int ba = __builtin_amdgcn_readlane(win_bid, i);
+    const int bb = __builtin_amdgcn_readlane(win_bid, i + 1);
+    r.a = ((int64_t)ba * a.Hkv + g) * kPageBytesG;
+    r.b = ((int64_t)bb * a.Hkv + g) * kPageBytesG;
     return r;
   };
   // Both rings have S stages.  Iteration jj (one barrier) consumes the TB tiles TB*jj ..
@@ -333,14 +343,17 @@ prefill_tiled_kernel(AttnArgs a, int runs_per_bg, int n_groups) {
   constexpr int kPerTile = T::kPerWave * (KEQV ? 1 : 2);
   constexpr int kWait = (S / TB - 2) * TB * kPerTile;  // copies of later iterations in flight
   const uint32_t vlane = 16u * lane;
+  // ring stage of tile t (t >= 0; S a power of two)
+  static_assert((S & (S - 1)) == 0, "ring depth a power of two");
+  auto stage = [](int t) { return (int)((unsigned)t & (unsigned)(S - 1)); };
   auto k_chunk = [&](int t, const TileIds& ids, int i) {
-    issue_chunk<D, KEQV, false, NW>(a, smem_off + T::kKRing + (t % S) * T::kTile, g, ids.a, ids.b,
-                                wave, i, vlane);
+    issue_chunk<D, KEQV, false, NW>(a, smem_off + T::kKRing + stage(t) * T::kTile, ids.a, ids.b,
+                                    wave, i, vlane);
   };
   auto v_chunk = [&](int t, const TileIds& ids, int i) {
     if constexpr (!KEQV)
-      issue_chunk<D, KEQV, true, NW>(a, smem_off + T::kVRing + (t % S) * T::kTile, g, ids.a,
-                                 ids.b, wave, i, vlane);
+      issue_chunk<D, KEQV, true, NW>(a, smem_off + T::kVRing + stage(t) * T::kTile, ids.a, ids.b,
+                                     wave, i, vlane);
   };
   auto issue_tile = [&](int t, const TileIds& ids) {
 #pragma unroll
@@ -354,9 +367,9 @@ prefill_tiled_kernel(AttnArgs a, int runs_per_bg, int n_groups) {
   auto process_tile = [&](int t, auto ncp, int ct, const TileIds* cids) {
     constexpr int Q = decltype(ncp)::value * T::kPerWave;  // copies of each ring
     const int k0 = (kt0 + t) * kTileKeys;
-    const unsigned char* kt = smem + T::kKRing + (t % S) * T::kTile;
-    const unsigned char* vt = smem + T::kVRing + (t % S) * T::kTile + voff;
-    const unsigned char* rt = smem + T::kRopeOff + (t % 2) * T::kRopeTile;
+    const unsigned char* kt = smem + T::kKRing + stage(t) * T::kTile;
+    const unsigned char* vt = smem + T::kVRing + stage(t) * T::kTile + voff;
+    const unsigned char* rt = smem + T::kRopeOff + ((unsigned)t & 1u) * T::kRopeTile;
     // K fragment f (chunk c = f / 2, product m = f % 2); exact K=V reads the chunks holding
     // dimensions 0-63 and their partners from the rotated copies
     auto kread = [&](auto fc) -> bf16x8_t {
@@ -527,7 +540,7 @@ prefill_tiled_kernel(AttnArgs a, int runs_per_bg, int n_groups) {
       if (tl >= TB * jj && tl < TB * jj + TB && (kt0 + tl) * kTileKeys + kTileKeys > L) {
         // slots of keys >= L may hold anything, NaN included, and a zero weight does not
         // cancel a NaN value: zero the values of those keys once, in LDS
-        zero_tail_values<D, KEQV, NW>(smem + (KEQV ? T::kKRing : T::kVRing) + (tl % S) * T::kTile,
+        zero_tail_values<D, KEQV, NW>(smem + (KEQV ? T::kKRing : T::kVRing) + stage(tl) * T::kTile,
                                   L - (kt0 + tl) * kTileKeys);
         __syncthreads();
       }
@@ -540,7 +553,7 @@ prefill_tiled_kernel(AttnArgs a, int runs_per_bg, int n_groups) {
       if (tl < np) {
         // source units rp_x and rp_x + D/16 of the K tile; in the rope buffer they become
         // columns rp_x and 8 + rp_x (row slots by k_slot of those columns)
-        const unsigned char* src = smem + T::kKRing + (tl % S) * T::kTile + rp_p * T::kPageBytes;
+        const unsigned char* src = smem + T::kKRing + stage(tl) * T::kTile + rp_p * T::kPageBytes;
         u32x4_t ua = *(const u32x4_t*)(src + 256 * rp_x + 16 * k_slot(rp_r, rp_x, rp_p));
         u32x4_t ub = *(const u32x4_t*)(src + 256 * (rp_x + D / 16) +
                                        16 * k_slot(rp_r, rp_x + D / 16, rp_p));
