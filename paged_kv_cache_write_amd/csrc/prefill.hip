@@ -306,19 +306,29 @@ prefill_tiled_kernel(AttnArgs a, int runs_per_bg, int n_groups) {
   // context aliases its first (its keys are masked and its values zeroed), so nothing past the
   // sequence's last page is read.  A window is loaded every 32 tiles.
   struct TileIds { int64_t a, b; };
-  int pw0 = -64;     // first page of the window (even; wave-uniform)
-  int win_bid = 0;   // this lane's block id in the window
+  int pw0 = -kWave, pwn = -kWave;  // first pages of the window and of the next one (even;
+                                   // wave-uniform)
+  int win_bid = 0, win_next = 0;   // this lane's block ids in them
   constexpr int64_t kPageBytesG = (int64_t)kPage * D * 2;
+  // pages past the context take the last page's id: the only one read is the second page of
+  // the last tile when last_page is even, which aliases the first
+  auto win_load = [&](int p0) -> int {
+    const int q = p0 + lane < last_page ? p0 + lane : last_page;
+    return (int)clamp_blk(a.bt[bt_row + bt_col(q, a.max_blocks, a.ring)], a.num_blocks);
+  };
   auto ids_of = [&](int tile) -> TileIds {
     TileIds r{0, 0};
     if (tile < 0 || tile >= ntiles) return r;
     const int page = 2 * (kt0 + tile);  // <= last_page for every tile of the range
     if (page < pw0 || page - pw0 >= kWave) {
-      // pages past the context take the last page's id: the only one read is the second page
-      // of the last tile when last_page is even, which aliases the first
+      win_bid = page == pwn ? win_next : win_load(page);
       pw0 = page;
-      const int q = page + lane < last_page ? page + lane : last_page;
-      win_bid = (int)clamp_blk(a.bt[bt_row + bt_col(q, a.max_blocks, a.ring)], a.num_blocks);
+    }
+    // the next window is loaded a quarter of a window before it is needed, so that its load
+    // has landed when the window moves
+    if (page - pw0 >= 3 * kWave / 4 && pwn != pw0 + kWave && pw0 + kWave <= last_page) {
+      pwn = pw0 + kWave;
+      win_next = win_load(pwn);
     }
     const int i = page - pw0;
     const int ba = __builtin_amdgcn_readlane(win_bid, i);
