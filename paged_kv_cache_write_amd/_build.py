@@ -27,13 +27,18 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
+# decode: the matrix-core accumulators are allocated in ordinary VGPRs.  Its kernels run one
+# wave per SIMD with up to 512 registers, and the softmax rescale multiplies the accumulators
+# with vector ALU instructions; with accumulation registers the compiler kept a VGPR copy of
+# every accumulator and moved all of them between the two files on every page.
+SOURCE_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(job) -> str:
     src, debug = job
     out = os.path.join(OBJ_DEBUG if debug else OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + (["-DGA_DEBUG_BOUNDS"] if debug else []) + \
-        ["-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [HIPCC] + FLAGS + SOURCE_FLAGS.get(src, []) + \
+        (["-DGA_DEBUG_BOUNDS"] if debug else []) + ["-c", os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}{' (debug)' if debug else ''}:\n{r.stderr}")

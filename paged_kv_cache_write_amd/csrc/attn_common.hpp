@@ -37,7 +37,7 @@ __device__ __forceinline__ u32x2_t ld8(const uint16_t* p) { return *(const u32x2
 template <int D>
 struct Acc {
   float4_t o[D / 16];
-  float m, l;
+  float m, l;  // the reference o and l are scaled to (exp2(-m)), and the weight sum
   __device__ __forceinline__ void init() {
 #pragma unroll
     for (int n = 0; n < D / 16; ++n) o[n] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -46,28 +46,45 @@ struct Acc {
   }
 };
 
+// Lazy online softmax: the reference of a row moves only when a weight exp2(x - m_ref) would
+// exceed 2^kLazyLog2.  Weights, row sums and O^T then stay below 2^64, 2^(64+log2 keys) and
+// 2^(64+log2 keys+log2 max|v|), far inside fp32 (and bf16) range, and rounding is relative,
+// so the size of a weight costs no precision; a large threshold makes the rescale of O^T (one
+// multiply per accumulator register) rare: the reference moves about once per row, on its
+// first visible keys.
+constexpr float kLazyLog2 = 64.0f;
+
 // Online softmax over NS new log2-domain scores per lane (the lane's row is its column c16;
-// its keys are spread over the 4 lane groups, hence the two xor steps for the max).
+// its keys are spread over the 4 lane groups, hence the two xor steps for the max), with the
+// lazily moved reference above: the accumulators are rescaled only in the rare step where
+// some lane's reference moves.  The weights come out as packed bf16 pairs (pw[w] holds keys
+// 2w, 2w+1), and the row sum adds those same rounded weights, so the numerator and the
+// denominator of the output use one set of weights.
 template <int D, int NS>
-__device__ __forceinline__ void softmax_update(Acc<D>& acc, const float (&x)[NS], float (&p)[NS]) {
+__device__ __forceinline__ void softmax_update(Acc<D>& acc, const float (&x)[NS],
+                                               uint32_t (&pw)[NS / 2]) {
   float mx = x[0];
 #pragma unroll
   for (int i = 1; i < NS; ++i) mx = fmaxf(mx, x[i]);
   mx = xor_max(mx, 16);
   mx = xor_max(mx, 32);
-  const float m_new = fmaxf(acc.m, mx);
-  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-  const float alpha = fast_exp2(acc.m - m_use);
-  float sum = 0.f;
+  const bool grow = mx > acc.m + kLazyLog2;
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    const float alpha = grow && acc.m != -INFINITY ? fast_exp2(acc.m - mx) : 1.f;
+    acc.l *= alpha;
 #pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    p[i] = fast_exp2(x[i] - m_use);
-    sum += p[i];
+    for (int n = 0; n < D / 16; ++n) acc.o[n] *= alpha;
+    if (grow) acc.m = mx;
   }
-  acc.l = acc.l * alpha + sum;
-  acc.m = m_new;
+  const float mu = acc.m == -INFINITY ? 0.f : acc.m;
+  float sum = acc.l;
 #pragma unroll
-  for (int n = 0; n < D / 16; ++n) acc.o[n] *= alpha;
+  for (int w = 0; w < NS / 2; ++w) {
+    const bf16x2_t b = cvt_bf16x2(fast_exp2(x[2 * w] - mu), fast_exp2(x[2 * w + 1] - mu));
+    sum = sum_bf16x2(b, sum);
+    pw[w] = __builtin_bit_cast(uint32_t, b);
+  }
+  acc.l = sum;
 }
 
 // Mask word for two bf16 slots: keep slot a (bits 0..15) / slot b (bits 16..31).

@@ -13,10 +13,12 @@
 // index w + s, which is unique, and the pieces of one segment are consecutive, so the merge
 // reads a contiguous range.
 //
-// Pipelining.  A worker keeps one step (two pages; one at head size 512 or with K=V) of K and V
-// in registers: the next step's K loads are issued as soon as the current step's QK^T products
-// have consumed K, and its V loads as soon as P.V has consumed V, so global loads stay in
-// flight while the softmax and matrix-core work of the current step run.  The block ids of a
+// Pipelining.  With separate K and V caches a worker keeps one step (two pages; one at head size
+// 512) of K and V in registers: the next step's K loads are issued as soon as the current step's
+// QK^T products have consumed K, and its V loads as soon as P.V has consumed V, so global loads
+// stay in flight while the softmax and matrix-core work of the current step run.  With K=V two
+// page buffers alternate, so two pages are always loading.  The softmax reference moves lazily,
+// so the accumulators are rescaled only in the rare step where it moves.  The block ids of a
 // piece are fetched 64 at a time into one lane-register each and read back with readlane.
 #include <atomic>
 #include <mutex>
@@ -41,83 +43,94 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-template <int D, bool KEQV>
-struct StepRegs {
-  static constexpr int NP = (KEQV || D == 512) ? 1 : 2;  // pages per step
-  u32x4_t k[NP][D / 32];
-  u32x2_t v[KEQV ? 1 : NP][KEQV ? 1 : D / 16];
+// The block ids of pages [pbeg, pbeg + np) of row b of the block table, 64 at a time in one
+// lane-register each: ensure(rel) makes page rel's window current (pages are visited in
+// increasing order) and prefetches the next window; id(rel) broadcasts page rel's block id.
+struct IdWindow {
+  const AttnArgs& a;
+  int64_t bt_row;
+  int pbeg, np, ids, ids_next, cur;
+  __device__ __forceinline__ IdWindow(const AttnArgs& a_, int b, int pbeg_, int np_)
+      : a(a_), bt_row((int64_t)b * a_.max_blocks), pbeg(pbeg_), np(np_), cur(0) {
+    ids = load(0);
+    ids_next = load(1);
+  }
+  // lane i of window c: page 64 c + i, clamped to the piece's last page (np >= 1), so the load
+  // needs no branch and no select; the ids are range-checked where they are used.  Together
+  // with the scheduling barrier in ensure() this lets the next window load straight into its
+  // register, so it is not waited for until its first page
+  __device__ __forceinline__ int load(int chunk) const {
+    const int i = min(chunk * 64 + (int)(threadIdx.x & 63), np - 1);
+    return a.bt[bt_row + bt_col(pbeg + i, a.max_blocks, a.ring)];
+  }
+  __device__ __forceinline__ void ensure(int rel) {
+    const int c = rel >> 6;
+    if (c != cur) {
+      ids = ids_next;
+      cur = c;
+      __builtin_amdgcn_sched_barrier(0);
+      ids_next = load(c + 1);
+    }
+  }
+  __device__ __forceinline__ int64_t id(int rel) const {
+    return clamp_blk(__builtin_amdgcn_readlane(ids, rel & 63), a.num_blocks);
+  }
 };
 
-// One piece: kv head g of sequence b, pages [pbeg, pend) (absolute page indices), visible keys
-// [lo, L).  Accumulates into acc.
-// EXACT (with KEQV): the stored keys are unrotated; the lane's two units of each of the first
-// two chunks (dimensions < 64, the ones exact mode may rotate) and their partners D/2 further
-// are rotated for QK^T (rho_x: the frequencies of their first pairs), while the values are
-// read unrotated.
-template <int D, bool CAP, bool KEQV, bool EXACT>
-__device__ __forceinline__ void decode_piece(const AttnArgs& a, const bf16x8_t (&qf)[D / 32],
-                                             Acc<D>& acc, int b, int g, int L, int lo,
-                                             int pbeg, int pend, uint16_t* lds,
-                                             const double (&rho_x)[2]) {
-  using R = StepRegs<D, KEQV>;
-  constexpr int NP = R::NP, NC = D / 32, ND = D / 16;
+// K unit (row c16, column 4c + j) of a page of logical parity par sits at row slot
+// c16 + 4 par + 4 ((c / 2) mod 2) of unit column 4c + j (the k_page_elem layout), i.e. at one
+// of three lane offsets; page bases are wave-uniform (scalar registers).
+struct KOffsets {
+  uint32_t o0, o1, o2;
+  __device__ __forceinline__ KOffsets() {
+    const int lane = threadIdx.x & 63, c16 = lane & 15, j = lane >> 4;
+    o0 = (uint32_t)(128 * j + 8 * c16);
+    o1 = (uint32_t)(128 * j + 8 * ((c16 + 4) & 15));
+    o2 = (uint32_t)(128 * j + 8 * ((c16 + 8) & 15));
+  }
+  template <int NC>
+  __device__ __forceinline__ void load(u32x4_t (&k)[NC], const uint16_t* kp, bool odd) const {
+    const uint32_t kA = odd ? o1 : o0, kB = odd ? o2 : o1;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) k[c] = ld16(kp + (((c >> 1) & 1) ? kB : kA) + 512 * c);
+  }
+};
+
+// One piece with separate K and V caches: kv head g of sequence b, pages [pbeg, pend)
+// (absolute page indices), visible keys [lo, L).  Accumulates into acc.  A step holds two
+// pages (one at head size 512) in registers: the next step's K loads are issued as soon as the
+// current step's QK^T products have consumed K, and its V loads as soon as P.V has consumed V.
+template <int D, bool CAP>
+__device__ __forceinline__ void decode_piece_kv(const AttnArgs& a, const bf16x8_t (&qf)[D / 32],
+                                                Acc<D>& acc, int b, int g, int L, int lo,
+                                                int pbeg, int pend) {
+  constexpr int NP = D == 512 ? 1 : 2, NC = D / 32, ND = D / 16;
   const int lane = threadIdx.x & 63, c16 = lane & 15, j = lane >> 4;
-  const int64_t bt_row = (int64_t)b * a.max_blocks;
   const int np = pend - pbeg;
   const int nsteps = (np + NP - 1) / NP;
-  const int64_t head_off = (int64_t)g;
-
-  auto load_ids = [&](int chunk) -> int {
-    const int i = chunk * 64 + lane;
-    return i < np ? (int)clamp_blk(a.bt[bt_row + bt_col(pbeg + i, a.max_blocks, a.ring)],
-                                   a.num_blocks)
-                  : 0;
-  };
-  int ids = load_ids(0);
-  int ids_next = np > 64 ? load_ids(1) : 0;
-  int cur_chunk = 0;
-  auto ensure_chunk = [&](int rel) {
-    const int c = rel >> 6;
-    if (c != cur_chunk) {
-      ids = ids_next;
-      cur_chunk = c;
-      ids_next = (c + 1) * 64 < np ? load_ids(c + 1) : 0;
-    }
-  };
+  IdWindow win(a, b, pbeg, np);
   auto blk_of = [&](int s, int p) -> int64_t {
     const int rel = s * NP + p;
-    const int r = rel < np ? rel : s * NP;  // a missing second page aliases the first (masked)
-    return (int64_t)__builtin_amdgcn_readlane(ids, r & 63);
+    return win.id(rel < np ? rel : s * NP);  // a missing second page aliases the first (masked)
   };
-
-  // page bases are wave-uniform (scalar registers); each lane adds one 32-bit offset
-  // K unit (row c16, column 4c + j) of a page of logical parity par: k_page_elem layout, row
-  // slot c16 + 4 par + 4 ((c / 2) mod 2), i.e. one of three lane offsets
-  const uint32_t koff0 = (uint32_t)(128 * j + 8 * c16);
-  const uint32_t koff1 = (uint32_t)(128 * j + 8 * ((c16 + 4) & 15));
-  const uint32_t koff2 = (uint32_t)(128 * j + 8 * ((c16 + 8) & 15));
+  const KOffsets ko;
   const uint32_t voff = (uint32_t)(c16 * kPage + 4 * j);
   const int64_t kpage = (int64_t)kPage * D;  // elements per (page, kv head)
-  R r;
+  u32x4_t k[NP][NC];
+  u32x2_t v[NP][ND];
   auto issue_k = [&](int s) {
-    ensure_chunk(s * NP);
+    win.ensure(s * NP);
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const uint16_t* kp = a.kc + (blk_of(s, p) * a.Hkv + head_off) * kpage;
-      const bool odd = ((pbeg + s * NP + p) & 1) != 0;
-      const uint32_t kA = odd ? koff1 : koff0, kB = odd ? koff2 : koff1;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) r.k[p][c] = ld16(kp + (((c >> 1) & 1) ? kB : kA) + 512 * c);
-    }
+    for (int p = 0; p < NP; ++p)
+      ko.load(k[p], a.kc + (blk_of(s, p) * a.Hkv + g) * kpage,
+              ((pbeg + s * NP + p) & 1) != 0);
   };
   auto issue_v = [&](int s) {
-    if constexpr (!KEQV) {
 #pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        const uint16_t* vp = a.vc + (blk_of(s, p) * a.Hkv + head_off) * kpage;
+    for (int p = 0; p < NP; ++p) {
+      const uint16_t* vp = a.vc + (blk_of(s, p) * a.Hkv + g) * kpage;
 #pragma unroll
-        for (int n = 0; n < ND; ++n) r.v[p][n] = ld8(vp + voff + n * 16 * kPage);
-      }
+      for (int n = 0; n < ND; ++n) v[p][n] = ld8(vp + voff + n * 16 * kPage);
     }
   };
 
@@ -126,58 +139,20 @@ __device__ __forceinline__ void decode_piece(const AttnArgs& a, const bf16x8_t (
     issue_v(0);
   }
   for (int s = 0; s < nsteps; ++s) {
-    const int pg0 = pbeg + s * NP;              // first page of the step
-    const int k0 = pg0 * kPage;
+    const int k0 = (pbeg + s * NP) * kPage;  // first key of the step
     const bool full = (s + 1) * NP <= np && k0 >= lo && k0 + NP * kPage <= L;
-    // exact K=V: the rotated copies of the rope units of this lane's key (row c16), as
-    // hi + lo bf16 terms
-    u32x4_t kr[2][2], kl[2][2];
-    if constexpr (EXACT) {
-      static_assert(KEQV && NP == 1, "exact K=V reads one page per step");
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        kr[c][0] = r.k[0][c];
-        kr[c][1] = r.k[0][c + NC / 2];
-        kl[c][0] = kl[c][1] = u32x4_t{0u, 0u, 0u, 0u};
-      }
-      if (a.rope_pairs > 0) {
-        const int64_t t = (int64_t)pg0 * kPage + c16;
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-          rope_units_exact(kr[c][0], kr[c][1], kl[c][0], kl[c][1], 4 * c + j, rho_x[c],
-                           a.rho_step, a.rope_pairs, t);
-      }
-    }
     // S^T = K Q^T for each page of the step
     float4_t sc[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       sc[p] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        u32x4_t kop = r.k[p][c];
-        if constexpr (EXACT) {
-          if (c < 2) {
-            kop = kr[c][0];
-            sc[p] = mfma_16x16x32(as_bf16x8(kl[c][0]), qf[c], sc[p]);
-          }
-          if (c >= NC / 2 && c < NC / 2 + 2) {
-            kop = kr[c - NC / 2][1];
-            sc[p] = mfma_16x16x32(as_bf16x8(kl[c - NC / 2][1]), qf[c], sc[p]);
-          }
-        }
-        sc[p] = mfma_16x16x32(as_bf16x8(kop), qf[c], sc[p]);
-      }
-    }
-    if constexpr (KEQV) {
-      // the page goes to this wave's LDS buffer for the transposed value reads
-      constexpr int S = KeqvLds<D>::kStride;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) *(u32x4_t*)(lds + c16 * S + 32 * c + 8 * j) = r.k[0][c];
+      for (int c = 0; c < NC; ++c) sc[p] = mfma_16x16x32(as_bf16x8(k[p][c]), qf[c], sc[p]);
     }
     if (s + 1 < nsteps) issue_k(s + 1);
 
-    float x[4 * NP], pr[4 * NP];
+    float x[4 * NP];
+    uint32_t pw[2 * NP];
     bool vk[4 * NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p)
@@ -196,56 +171,150 @@ __device__ __forceinline__ void decode_piece(const AttnArgs& a, const bf16x8_t (
           if (!ok) x[4 * p + i] = -INFINITY;
           vk[4 * p + i] = ok;
         }
+      // values of keys outside the range may be anything (NaN included): zero them, since a
+      // zero weight does not cancel a NaN in the product
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const uint32_t m01 = keep2(vk[4 * p], vk[4 * p + 1]);
+        const uint32_t m23 = keep2(vk[4 * p + 2], vk[4 * p + 3]);
+#pragma unroll
+        for (int n = 0; n < ND; ++n) {
+          v[p][n].x &= m01;
+          v[p][n].y &= m23;
+        }
+      }
     }
-    softmax_update<D, 4 * NP>(acc, x, pr);
+    softmax_update<D, 4 * NP>(acc, x, pw);
 
-    if constexpr (!KEQV) {
-      if constexpr (NP == 2) {
-        const bf16x8_t pf =
-            as_bf16x8(u32x4_t{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
-                              pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])});
-        const uint32_t mA01 = keep2(vk[0], vk[1]), mA23 = keep2(vk[2], vk[3]);
-        const uint32_t mB01 = keep2(vk[4], vk[5]), mB23 = keep2(vk[6], vk[7]);
+    if constexpr (NP == 2) {
+      const bf16x8_t pf = as_bf16x8(u32x4_t{pw[0], pw[1], pw[2], pw[3]});
 #pragma unroll
-        for (int n = 0; n < ND; ++n) {
-          u32x2_t va = r.v[0][n], vb = r.v[1][n];
-          if (!full) {
-            va.x &= mA01; va.y &= mA23;
-            vb.x &= mB01; vb.y &= mB23;
-          }
-          acc.o[n] = mfma_16x16x32(as_bf16x8(u32x4_t{va.x, va.y, vb.x, vb.y}), pf, acc.o[n]);
-        }
-      } else {
-        const short4_t pf =
-            as_short4(u32x2_t{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])});
-        const uint32_t m01 = keep2(vk[0], vk[1]), m23 = keep2(vk[2], vk[3]);
-#pragma unroll
-        for (int n = 0; n < ND; ++n) {
-          u32x2_t va = r.v[0][n];
-          if (!full) { va.x &= m01; va.y &= m23; }
-          acc.o[n] = mfma_16x16x16(as_short4(va), pf, acc.o[n]);
-        }
-      }
-      if (s + 1 < nsteps) issue_v(s + 1);
+      for (int n = 0; n < ND; ++n)
+        acc.o[n] = mfma_16x16x32(
+            as_bf16x8(u32x4_t{v[0][n].x, v[0][n].y, v[1][n].x, v[1][n].y}), pf, acc.o[n]);
     } else {
-      constexpr int S = KeqvLds<D>::kStride;
-      const short4_t pf = as_short4(u32x2_t{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])});
-      wave_lds_sync();
-      // V^T fragment (d = 16 n + c16, keys 4j .. 4j+3) by one transposing read: lane 4e + q
-      // of a group points at dimensions 16 n + 4q .. + 3 of key 4j + e
-      const uint16_t* col = lds + (4 * j + (c16 >> 2)) * S + 4 * (c16 & 3);
-      const uint32_t m01 = keep2(vk[0], vk[1]), m23 = keep2(vk[2], vk[3]);
+      const short4_t pf = as_short4(u32x2_t{pw[0], pw[1]});
 #pragma unroll
-      for (int n = 0; n < ND; ++n) {
-        u32x2_t av = lds_read_tr16(col + 16 * n);
-        if (!full) {
-          av.x &= m01;
-          av.y &= m23;
-        }
-        acc.o[n] = mfma_16x16x16(as_short4(av), pf, acc.o[n]);
-      }
-      wave_lds_sync();
+      for (int n = 0; n < ND; ++n) acc.o[n] = mfma_16x16x16(as_short4(v[0][n]), pf, acc.o[n]);
     }
+    if (s + 1 < nsteps) issue_v(s + 1);
+  }
+}
+
+// One piece with K=V: the cached page serves as keys and, through this wave's LDS copy, as
+// values.  Pages are computed one at a time from two register buffers that alternate, so the
+// loads of the page after next are issued as soon as a page's QK^T products and LDS copy have
+// consumed its buffer: two pages stay in flight per wave.
+// EXACT: the stored keys are unrotated; the lane's two units of each of the first two chunks
+// (dimensions < 64, the ones exact mode may rotate) and their partners D/2 further are
+// rotated for QK^T (rho_x: the frequencies of their first pairs), while the values are read
+// unrotated.
+template <int D, bool CAP, bool EXACT>
+__device__ __forceinline__ void decode_piece_keqv(const AttnArgs& a,
+                                                  const bf16x8_t (&qf)[D / 32], Acc<D>& acc,
+                                                  int b, int g, int L, int lo, int pbeg,
+                                                  int pend, uint16_t* lds,
+                                                  const double (&rho_x)[2]) {
+  constexpr int NC = D / 32, ND = D / 16, S = KeqvLds<D>::kStride;
+  const int lane = threadIdx.x & 63, c16 = lane & 15, j = lane >> 4;
+  const int np = pend - pbeg;
+  IdWindow win(a, b, pbeg, np);
+  const KOffsets ko;
+  const int64_t kpage = (int64_t)kPage * D;  // elements per (page, kv head)
+  auto issue = [&](u32x4_t (&k)[NC], int s) {
+    win.ensure(s);
+    ko.load(k, a.kc + (win.id(s) * a.Hkv + g) * kpage, ((pbeg + s) & 1) != 0);
+  };
+  // this lane writes the units 4c + j of key row c16; the V^T fragment (d = 16 n + c16, keys
+  // 4j .. 4j+3) is one transposing read, lane 4e + q of a group pointing at dimensions
+  // 16 n + 4q .. + 3 of key 4j + e
+  uint16_t* const row_lds = lds + c16 * S + 8 * j;
+  const uint16_t* const col = lds + (4 * j + (c16 >> 2)) * S + 4 * (c16 & 3);
+
+  // step s computes page s of the piece from buffer k and then reloads k with page s + 2.  The
+  // loads are issued on every step, so the count of loads issued after a buffer's is the same
+  // on every path and the wait for a buffer leaves the other one in flight: past the piece's
+  // end a step reloads its own page (a cache hit), and a step past the end (s = np, odd np)
+  // has every key masked.
+  auto step = [&](u32x4_t (&k)[NC], int s) {
+    const int k0 = (pbeg + s) * kPage;  // first key of the page
+    const bool inside = s < np;
+    const bool full = inside && k0 >= lo && k0 + kPage <= L;
+    // exact K=V: the rotated copies of the rope units of this lane's key (row c16), as
+    // hi + lo bf16 terms
+    u32x4_t kr[2][2], kl[2][2];
+    if constexpr (EXACT) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        kr[c][0] = k[c];
+        kr[c][1] = k[c + NC / 2];
+        kl[c][0] = kl[c][1] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+      if (a.rope_pairs > 0) {
+        const int64_t t = (int64_t)k0 + c16;
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          rope_units_exact(kr[c][0], kr[c][1], kl[c][0], kl[c][1], 4 * c + j, rho_x[c],
+                           a.rho_step, a.rope_pairs, t);
+      }
+    }
+    // S^T = K Q^T
+    float4_t sc = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      u32x4_t kop = k[c];
+      if constexpr (EXACT) {
+        if (c < 2) {
+          kop = kr[c][0];
+          sc = mfma_16x16x32(as_bf16x8(kl[c][0]), qf[c], sc);
+        }
+        if (c >= NC / 2 && c < NC / 2 + 2) {
+          kop = kr[c - NC / 2][1];
+          sc = mfma_16x16x32(as_bf16x8(kl[c - NC / 2][1]), qf[c], sc);
+        }
+      }
+      sc = mfma_16x16x32(as_bf16x8(kop), qf[c], sc);
+    }
+    // the page to this wave's LDS buffer (the previous page's value reads have completed);
+    // a key outside the range gets a zero row there, since its value may be anything (NaN
+    // included) and a zero weight does not cancel a NaN in the product
+#pragma unroll
+    for (int c = 0; c < NC; ++c) *(u32x4_t*)(row_lds + 32 * c) = k[c];
+    if (!full && (!inside || k0 + c16 < lo || k0 + c16 >= L)) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) *(u32x4_t*)(row_lds + 32 * c) = u32x4_t{0u, 0u, 0u, 0u};
+    }
+    issue(k, s + 2 < np ? s + 2 : (s < np ? s : np - 1));
+
+    float x[4];
+    uint32_t pw[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = to_log2<CAP>(sc[i], a.sc);
+    if (!full) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = k0 + 4 * j + i;
+        if (!inside || key < lo || key >= L) x[i] = -INFINITY;
+      }
+    }
+    softmax_update<D, 4>(acc, x, pw);
+    const short4_t pf = as_short4(u32x2_t{pw[0], pw[1]});
+    wave_lds_sync();
+    u32x2_t av[ND];
+#pragma unroll
+    for (int n = 0; n < ND; ++n) av[n] = lds_read_tr16(col + 16 * n);
+#pragma unroll
+    for (int n = 0; n < ND; ++n) acc.o[n] = mfma_16x16x16(as_short4(av[n]), pf, acc.o[n]);
+    wave_lds_sync();
+  };
+
+  if (np <= 0) return;
+  u32x4_t kA[NC], kB[NC];
+  issue(kA, 0);
+  issue(kB, np > 1 ? 1 : 0);
+  for (int s = 0; s < np; s += 2) {
+    step(kA, s);
+    step(kB, s + 1);
   }
 }
 
@@ -346,8 +415,11 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(AttnArgs a) {
     load_q<D>(qf, a.q + ((int64_t)b * a.Hq + g * G + (head_ok ? c16 : 0)) * D, head_ok);
     Acc<D> acc;
     acc.init();
-    decode_piece<D, CAP, KEQV, EXACT>(a, qf, acc, b, g, L, lo, p0 + lp, p0 + lp + cnt, lds,
-                                      rho_x);
+    if constexpr (KEQV)
+      decode_piece_keqv<D, CAP, EXACT>(a, qf, acc, b, g, L, lo, p0 + lp, p0 + lp + cnt, lds,
+                                       rho_x);
+    else
+      decode_piece_kv<D, CAP>(a, qf, acc, b, g, L, lo, p0 + lp, p0 + lp + cnt);
     acc.l += __shfl_xor(acc.l, 16, kWave);
     acc.l += __shfl_xor(acc.l, 32, kWave);
     const int64_t row = ((int64_t)worker + (int64_t)b * Hkv + g) * G + c16;

@@ -1,6 +1,5 @@
-// prefill_common.hpp -- pieces shared by the prefill kernels: tile size, the lazy softmax
-// threshold, the key order of the QK^T products, and the HBM -> LDS copy, scalar-load and
-// wait primitives.
+// prefill_common.hpp -- pieces shared by the prefill kernels: tile size, the key order of the
+// QK^T products, and the HBM -> LDS copy, scalar-load and wait primitives.
 #pragma once
 
 #include <utility>
@@ -10,14 +9,6 @@
 namespace ga {
 
 constexpr int kTileKeys = 2 * kPage;  // 32 keys per tile: P.V runs on 16x16x32 MFMAs
-
-// Lazy online softmax: the reference of a row moves only when a weight exp2(x - m_ref) would
-// exceed 2^kLazyLog2.  Weights, row sums and O^T then stay below 2^64, 2^(64+log2 keys) and
-// 2^(64+log2 keys+log2 max|v|), far inside fp32 (and bf16) range, and rounding is relative,
-// so the size of a weight costs no precision; a large threshold makes the rescale of O^T (one
-// multiply per accumulator register) rare: the reference moves about once per row, on its
-// first visible tile.
-constexpr float kLazyLog2 = 64.0f;
 
 // How raw scores s = q.k enter the softmax (exponentials are base 2):
 //   kScorePlain  x = s * scale * log2(e);      weight exp2(x - mu)
