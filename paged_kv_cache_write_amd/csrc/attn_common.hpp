@@ -55,7 +55,7 @@ struct Acc {
 constexpr float kLazyLog2 = 64.0f;
 
 // Online softmax over NS new log2-domain scores per lane (the lane's row is its column c16;
-// its keys are spread over the 4 lane groups, hence the two xor steps for the max), with the
+// its keys are spread over the 4 lane groups, hence the max over the groups), with the
 // lazily moved reference above: the accumulators are rescaled only in the rare step where
 // some lane's reference moves.  The weights come out as packed bf16 pairs (pw[w] holds keys
 // 2w, 2w+1), and the row sum adds those same rounded weights, so the numerator and the
@@ -66,8 +66,7 @@ __device__ __forceinline__ void softmax_update(Acc<D>& acc, const float (&x)[NS]
   float mx = x[0];
 #pragma unroll
   for (int i = 1; i < NS; ++i) mx = fmaxf(mx, x[i]);
-  mx = xor_max(mx, 16);
-  mx = xor_max(mx, 32);
+  mx = max_over_groups(mx);
   const bool grow = mx > acc.m + kLazyLog2;
   if (__builtin_amdgcn_ballot_w64(grow) != 0) {
     const float alpha = grow && acc.m != -INFINITY ? fast_exp2(acc.m - mx) : 1.f;

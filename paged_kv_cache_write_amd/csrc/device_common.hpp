@@ -174,9 +174,6 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // ------------------------------------------------------------------------ cross-lane -------
 
-__device__ __forceinline__ float xor_max(float v, int mask) {
-  return fmaxf(v, __shfl_xor(v, mask, kWave));
-}
 // Max over the 4 lane groups (lanes c, c+16, c+32, c+48) without LDS: the two permlane swaps
 // exchange rows of 16 and halves of 32 lanes.
 __device__ __forceinline__ float max_over_groups(float v) {

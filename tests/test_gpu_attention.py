@@ -182,8 +182,8 @@ def test_decode_equals_last_prefill_row_and_gqa_equals_repeated_heads():
     last = torch.from_numpy(cu[1:] - 1).long().cuda()
     dec = case.decode(qd[last].contiguous(), cl)
     torch.cuda.synchronize()
-    # the rounding bound, from the stored bytes: decode's row sum adds unrounded weights,
-    # prefill's the bf16-rounded ones
+    # the rounding bound, from the stored bytes: both kernels' row sums add the same
+    # bf16-rounded weights that multiply V
     kc, vc = case.host_caches()
     K = logical_k(kc, pb.block_table, lens, unit_elems("bf16"))
     f32 = lambda a: (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
@@ -198,8 +198,7 @@ def test_decode_equals_last_prefill_row_and_gqa_equals_repeated_heads():
             Kb, Vb = K[blk, g, r, :], V[blk, g, :, r]
             w = softmax_weights(qn[b, h], Kb, spec.scale, spec.softcap)
             out = w @ Vb
-            sigma[b, h] = (weight_rounding_sigma(w, Vb, 0.0) +
-                           weight_rounding_sigma(w, Vb, out))
+            sigma[b, h] = 2.0 * weight_rounding_sigma(w, Vb, out)
     assert_within_rounding_bound(dec, pre[last], sigma)
     # GQA: the same layer with each kv head repeated 4x (MHA) gives the same bits
     spec2 = wl.LayerSpec("bf16", 8, 8, 256, window=50, rope_theta=1e4)
