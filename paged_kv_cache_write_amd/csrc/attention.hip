@@ -14,8 +14,11 @@ namespace {
 
 // ---------------------------------------------------------------------------- fp32 -------
 
-// Plain fp32 path (one wavefront per (query, head), one key at a time, fp32 everywhere):
-// used for float caches, where the matrix cores would not keep fp32 products exact.
+// Plain fp32 path (one workgroup per (query, head), fp32 everywhere): used for float caches,
+// where the matrix cores would not keep fp32 products exact.  The 4 waves take turns over the
+// steps of kF32Keys keys (wave w the steps w, w + 4, ..) with online softmaxes of their own,
+// which are merged at the end through LDS.
+constexpr int kF32Keys = 8;  // keys per step of the key loop
 template <int D>
 __global__ __launch_bounds__(256) void attn_f32_kernel(const float* q, const int32_t* cu,
                                                        const float* kc, const float* vc,
@@ -29,8 +32,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* q, const int
                                                        float rope_theta, float rope_scale,
                                                        const float* kv_kw, const float* kv_vw) {
   constexpr int C = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t wid = blockIdx.x;
   const int rq = (int)(wid / Hq), h = (int)(wid - (wid / Hq) * Hq);
   if (rq >= total_q) return;
   int b, i, n;
@@ -78,65 +81,131 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* q, const int
                    ? pow((double)rope_theta, -2.0 * k / (double)D) / (double)rope_scale
                    : 0.0;
   }
+  // Keys go U at a time: their loads are issued together, then their scores are reduced and
+  // folded into the running softmax at once, so a key costs a fraction of a memory round trip.
+  // The block ids of 64 pages at a time sit one per lane and are broadcast with readlane.
+  int key_end = t;
+  if (!ring && t / kPage >= max_blocks) {
+    debug_flag(kDbgBound);
+    key_end = max_blocks * kPage - 1;
+  }
+  const int64_t bt_row = (int64_t)b * max_blocks;
+  const int p_last = key_end / kPage;
+  auto ids_at = [&](int pw) -> int {  // lane i: block id of page pw + i (clamped)
+    const int p = pw + lane < p_last ? pw + lane : p_last;
+    return bt[bt_row + bt_col(p, max_blocks, ring)];
+  };
+  int pw = lo / kPage;
+  int ids = ids_at(pw);
   float m = -INFINITY, l = 0.f;
-  for (int key = lo; key <= t; ++key) {
-    const int page = key / kPage;
-    if (!ring && page >= max_blocks) {
-      debug_flag(kDbgBound);
-      break;
+  for (int k0 = lo + wave * kF32Keys; k0 <= key_end; k0 += 4 * kF32Keys) {
+    const int k_last = k0 + kF32Keys - 1 < key_end ? k0 + kF32Keys - 1 : key_end;
+    if (k_last / kPage - pw >= kWave) {  // the step's pages leave the window: move it
+      pw = k0 / kPage;
+      ids = ids_at(pw);
     }
-    const int64_t blk =
-        clamp_blk(bt[(int64_t)b * max_blocks + bt_col(page, max_blocks, ring)], num_blocks);
-    const int off = key - page * kPage;
-    const float* kp = kc + (blk * Hkv + g) * kPage * D;  // K page (k_page_elem layout)
-    float kv[C];
+    // every load of the step is issued before any is used (the values' select between the
+    // K and the V cache waits for the scores)
+    float kv[kF32Keys][C], vv[kF32Keys][C];
 #pragma unroll
-    for (int e = 0; e < C; ++e) kv[e] = kp[k_page_elem<4>(off, lane * C + e, page)];
-    float ks[C];  // the key as the scores see it
+    for (int u = 0; u < kF32Keys; ++u) {
+      // keys past the range alias the last one (real data; their weights are zero)
+      const int key = k0 + u < key_end ? k0 + u : key_end;
+      const int page = key / kPage, off = key - page * kPage;
+      const int64_t blk = clamp_blk(__builtin_amdgcn_readlane(ids, page - pw), num_blocks);
+      const float* kp = kc + (blk * Hkv + g) * kPage * D;  // K page (k_page_elem layout)
 #pragma unroll
-    for (int e = 0; e < C; ++e) ks[e] = kv[e];
-    if (exact && rope_pairs > 0) {
+      for (int e = 0; e < C; ++e) kv[u][e] = kp[k_page_elem<4>(off, lane * C + e, page)];
+      // (with K=V the loads read the K page instead, and go unused: no branch between them)
+      const float* vp = k_eq_v ? kp : vc + ((blk * Hkv + g) * D + lane * C) * kPage + off;
 #pragma unroll
-      for (int e = 0; e < C; ++e) {
-        const float partner = __shfl_xor(kv[e], 32, kWave);
-        double sn, cs;
-        sincos((double)key * omega[e], &sn, &cs);
-        ks[e] = first_half ? (float)((double)kv[e] * cs - (double)partner * sn)
-                           : (float)((double)kv[e] * cs + (double)partner * sn);
+      for (int e = 0; e < C; ++e) vv[u][e] = vp[e * kPage];
+    }
+    float part[kF32Keys];
+#pragma unroll
+    for (int u = 0; u < kF32Keys; ++u) {
+      float ks[C];  // the key as the scores see it
+#pragma unroll
+      for (int e = 0; e < C; ++e) ks[e] = kv[u][e];
+      if (exact && rope_pairs > 0) {
+        const int key = k0 + u < key_end ? k0 + u : key_end;
+#pragma unroll
+        for (int e = 0; e < C; ++e) {
+          const float partner = __shfl_xor(kv[u][e], 32, kWave);
+          double sn, cs;
+          sincos((double)key * omega[e], &sn, &cs);
+          ks[e] = first_half ? (float)((double)kv[u][e] * cs - (double)partner * sn)
+                             : (float)((double)kv[u][e] * cs + (double)partner * sn);
+        }
       }
+      part[u] = 0.f;
+#pragma unroll
+      for (int e = 0; e < C; ++e) part[u] = fmaf(qv[e], ks[e], part[u]);
     }
-    float part = 0.f;
 #pragma unroll
-    for (int e = 0; e < C; ++e) part = fmaf(qv[e], ks[e], part);
+    for (int msk = 32; msk >= 1; msk >>= 1)
 #pragma unroll
-    for (int msk = 32; msk >= 1; msk >>= 1) part += __shfl_xor(part, msk, kWave);
-    float sc = part * scale;
-    if (cap > 0.f) sc = cap * tanhf(sc / cap);
-    const float m_new = fmaxf(m, sc);
-    const float alpha = expf(m - m_new);
-    const float pw = expf(sc - m_new);
-    l = l * alpha + pw;
+      for (int u = 0; u < kF32Keys; ++u) part[u] += __shfl_xor(part[u], msk, kWave);
+    float sc[kF32Keys];
+    float m_new = m;
 #pragma unroll
-    for (int e = 0; e < C; ++e) {
-      const float vv = k_eq_v ? kv[e] : vc[((blk * Hkv + g) * D + lane * C + e) * kPage + off];
-      o[e] = o[e] * alpha + pw * vv;
+    for (int u = 0; u < kF32Keys; ++u) {
+      float x = part[u] * scale;
+      if (cap > 0.f) x = cap * tanhf(x / cap);
+      sc[u] = k0 + u <= key_end ? x : -INFINITY;
+      m_new = fmaxf(m_new, sc[u]);
+    }
+    const float alpha = expf(m - m_new);  // m = -inf on the first step: 0
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < C; ++e) o[e] *= alpha;
+#pragma unroll
+    for (int u = 0; u < kF32Keys; ++u) {
+      const float pw_u = expf(sc[u] - m_new);
+      l += pw_u;
+#pragma unroll
+      for (int e = 0; e < C; ++e) o[e] = fmaf(pw_u, k_eq_v ? kv[u][e] : vv[u][e], o[e]);
     }
     m = m_new;
   }
+  // merge the 4 waves' softmaxes: out = sum_w o_w e^(m_w - M) / sum_w l_w e^(m_w - M) (a
+  // wave without keys has m = -inf and weight 0; wave 0 always has keys)
+  __shared__ float red_ml[4][2];
+  __shared__ float red_o[4][D];
+  if (lane == 0) {
+    red_ml[wave][0] = m;
+    red_ml[wave][1] = l;
+  }
+#pragma unroll
+  for (int e = 0; e < C; ++e) red_o[wave][lane * C + e] = o[e];
+  __syncthreads();
+  if (wave != 0) return;
+  float M = red_ml[0][0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) M = fmaxf(M, red_ml[w][0]);
+  float lsum = 0.f, ow[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    ow[w] = expf(red_ml[w][0] - M);
+    lsum += ow[w] * red_ml[w][1];
+  }
 #pragma unroll
   for (int e = 0; e < C; ++e) {
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) acc += ow[w] * red_o[w][lane * C + e];
     float f = 1.f;  // exact K=V: values are the stored keys times w_v / w_k
     if (kv_vw) f = kv_vw[lane * C + e] / kv_kw[lane * C + e];
-    dst[e] = o[e] / l * f;
+    dst[e] = acc / lsum * f;
   }
 }
 
 template <int D>
 hipError_t launch_f32_t(const AttnLaunch& L, bool decode, hipStream_t s) {
   const int total_q = decode ? L.batch : L.total_q;
-  const int64_t waves = (int64_t)total_q * L.Hq;
-  const int64_t blocks = (waves + 3) / 4;
+  const int64_t blocks = (int64_t)total_q * L.Hq;  // one workgroup per (query, head)
   if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((attn_f32_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, s,
                      (const float*)L.q, L.cu_seqlens_q, (const float*)L.k_cache,
                      (const float*)L.v_cache, L.block_table, L.context_lens, (float*)L.out,
