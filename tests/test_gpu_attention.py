@@ -36,6 +36,9 @@ DECODE_CASES = [
     ("bf16", 16, 1, 256, 0, 0.0, False, [129, 1000]),
     ("fp32", 4, 2, 256, 128, 0.0, False, [1, 128, 129, 272]),
     ("fp32", 8, 2, 512, 0, 20.0, True, [3, 150]),
+    # fp32 past 64 pages of keys: the kernel's window of block ids moves
+    ("fp32", 4, 2, 256, 0, 0.0, False, [1100, 2500]),
+    ("fp32", 4, 1, 128, 1500, 10.0, True, [1700, 3000, 1023]),
 ]
 
 
@@ -79,6 +82,9 @@ PREFILL_CASES = [
     ("bf16", 8, 4, 256, 24, 0.0, False, ([50, 30, 64], [20, 0, 64])),
     ("fp32", 4, 2, 256, 128, 0.0, False, ([256], [256])),
     ("fp32", 8, 2, 512, 0, 0.0, True, ([90, 31], [30, 31])),
+    # fp32 past 64 pages of keys (the window of block ids moves), global and sliding
+    ("fp32", 4, 2, 256, 0, 0.0, False, ([2200, 1500], [24, 40])),
+    ("fp32", 4, 2, 128, 1100, 0.0, False, ([2300], [37])),
 ]
 
 
