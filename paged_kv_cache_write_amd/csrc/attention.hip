@@ -98,28 +98,32 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* q, const int
   int pw = lo / kPage;
   int ids = ids_at(pw);
   float m = -INFINITY, l = 0.f;
-  for (int k0 = lo + wave * kF32Keys; k0 <= key_end; k0 += 4 * kF32Keys) {
-    const int k_last = k0 + kF32Keys - 1 < key_end ? k0 + kF32Keys - 1 : key_end;
-    if (k_last / kPage - pw >= kWave) {  // the step's pages leave the window: move it
-      pw = k0 / kPage;
+  // steps start at multiples of kF32Keys, so a step's keys lie in one page; keys of a step
+  // outside [lo, key_end] are masked (their slots hold written keys, or anything past L)
+  static_assert(kPage % kF32Keys == 0, "a step within one page");
+  for (int k0 = (lo & ~(kF32Keys - 1)) + wave * kF32Keys; k0 <= key_end; k0 += 4 * kF32Keys) {
+    const int page = k0 / kPage, off0 = k0 - page * kPage;
+    if (page - pw >= kWave) {  // the step's page leaves the window: move it
+      pw = page;
       ids = ids_at(pw);
     }
-    // every load of the step is issued before any is used (the values' select between the
-    // K and the V cache waits for the scores)
-    float kv[kF32Keys][C], vv[kF32Keys][C];
+    const int64_t blk = clamp_blk(__builtin_amdgcn_readlane(ids, page - pw), num_blocks);
+    const float* kp = kc + (blk * Hkv + g) * kPage * D;  // K page (k_page_elem layout)
+    // every load of the step is issued before any is used
+    float kv[kF32Keys][C];
 #pragma unroll
-    for (int u = 0; u < kF32Keys; ++u) {
-      // keys past the range alias the last one (real data; their weights are zero)
-      const int key = k0 + u < key_end ? k0 + u : key_end;
-      const int page = key / kPage, off = key - page * kPage;
-      const int64_t blk = clamp_blk(__builtin_amdgcn_readlane(ids, page - pw), num_blocks);
-      const float* kp = kc + (blk * Hkv + g) * kPage * D;  // K page (k_page_elem layout)
+    for (int u = 0; u < kF32Keys; ++u)
 #pragma unroll
-      for (int e = 0; e < C; ++e) kv[u][e] = kp[k_page_elem<4>(off, lane * C + e, page)];
-      // (with K=V the loads read the K page instead, and go unused: no branch between them)
-      const float* vp = k_eq_v ? kp : vc + ((blk * Hkv + g) * D + lane * C) * kPage + off;
+      for (int e = 0; e < C; ++e) kv[u][e] = kp[k_page_elem<4>(off0 + u, lane * C + e, page)];
+    // values: dimension d of the step's keys is kF32Keys consecutive floats of the V^T page
+    // (with K=V the loads read the K page instead and go unused: no branch between them)
+    float4_t vq[C][kF32Keys / 4];
 #pragma unroll
-      for (int e = 0; e < C; ++e) vv[u][e] = vp[e * kPage];
+    for (int e = 0; e < C; ++e) {
+      const float* vp = k_eq_v ? kp + 4 * kF32Keys * e
+                               : vc + ((blk * Hkv + g) * D + lane * C + e) * kPage + off0;
+#pragma unroll
+      for (int w = 0; w < kF32Keys / 4; ++w) vq[e][w] = ((const float4_t*)vp)[w];
     }
     float part[kF32Keys];
 #pragma unroll
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* q, const int
 #pragma unroll
       for (int e = 0; e < C; ++e) ks[e] = kv[u][e];
       if (exact && rope_pairs > 0) {
-        const int key = k0 + u < key_end ? k0 + u : key_end;
+        const int key = k0 + u;
 #pragma unroll
         for (int e = 0; e < C; ++e) {
           const float partner = __shfl_xor(kv[u][e], 32, kWave);
@@ -152,7 +156,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* q, const int
     for (int u = 0; u < kF32Keys; ++u) {
       float x = part[u] * scale;
       if (cap > 0.f) x = cap * tanhf(x / cap);
-      sc[u] = k0 + u <= key_end ? x : -INFINITY;
+      sc[u] = k0 + u >= lo && k0 + u <= key_end ? x : -INFINITY;
       m_new = fmaxf(m_new, sc[u]);
     }
     const float alpha = expf(m - m_new);  // m = -inf on the first step: 0
@@ -161,10 +165,15 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* q, const int
     for (int e = 0; e < C; ++e) o[e] *= alpha;
 #pragma unroll
     for (int u = 0; u < kF32Keys; ++u) {
+      const bool in = k0 + u >= lo && k0 + u <= key_end;
       const float pw_u = expf(sc[u] - m_new);
       l += pw_u;
+      // a masked key's slot may hold anything, NaN included: its value is replaced by 0
 #pragma unroll
-      for (int e = 0; e < C; ++e) o[e] = fmaf(pw_u, k_eq_v ? kv[u][e] : vv[u][e], o[e]);
+      for (int e = 0; e < C; ++e) {
+        const float vval = k_eq_v ? kv[u][e] : vq[e][u / 4][u % 4];
+        o[e] = fmaf(pw_u, in ? vval : 0.f, o[e]);
+      }
     }
     m = m_new;
   }
