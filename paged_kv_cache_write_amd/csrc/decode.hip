@@ -88,11 +88,14 @@ struct KOffsets {
     o1 = (uint32_t)(128 * j + 8 * ((c16 + 4) & 15));
     o2 = (uint32_t)(128 * j + 8 * ((c16 + 8) & 15));
   }
+  // stride 512 loads the page's units; stride 0 loads the first 1 KiB NC times (a load that
+  // only keeps the count of loads in flight the same)
   template <int NC>
-  __device__ __forceinline__ void load(u32x4_t (&k)[NC], const uint16_t* kp, bool odd) const {
+  __device__ __forceinline__ void load(u32x4_t (&k)[NC], const uint16_t* kp, bool odd,
+                                       uint32_t stride = 512) const {
     const uint32_t kA = odd ? o1 : o0, kB = odd ? o2 : o1;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) k[c] = ld16(kp + (((c >> 1) & 1) ? kB : kA) + 512 * c);
+    for (int c = 0; c < NC; ++c) k[c] = ld16(kp + (((c >> 1) & 1) ? kB : kA) + stride * c);
   }
 };
 
@@ -221,9 +224,10 @@ __device__ __forceinline__ void decode_piece_keqv(const AttnArgs& a,
   IdWindow win(a, b, pbeg, np);
   const KOffsets ko;
   const int64_t kpage = (int64_t)kPage * D;  // elements per (page, kv head)
-  auto issue = [&](u32x4_t (&k)[NC], int s) {
+  auto issue = [&](u32x4_t (&k)[NC], int s, bool real) {
     win.ensure(s);
-    ko.load(k, a.kc + (win.id(s) * a.Hkv + g) * kpage, ((pbeg + s) & 1) != 0);
+    ko.load(k, a.kc + (win.id(s) * a.Hkv + g) * kpage, ((pbeg + s) & 1) != 0,
+            real ? 512u : 0u);
   };
   // this lane writes the units 4c + j of key row c16; the V^T fragment (d = 16 n + c16, keys
   // 4j .. 4j+3) is one transposing read, lane 4e + q of a group pointing at dimensions
@@ -234,8 +238,8 @@ __device__ __forceinline__ void decode_piece_keqv(const AttnArgs& a,
   // step s computes page s of the piece from buffer k and then reloads k with page s + 2.  The
   // loads are issued on every step, so the count of loads issued after a buffer's is the same
   // on every path and the wait for a buffer leaves the other one in flight: past the piece's
-  // end a step reloads its own page (a cache hit), and a step past the end (s = np, odd np)
-  // has every key masked.
+  // end a step loads the first 1 KiB of its own page NC times (data no step uses unmasked),
+  // and a step past the end (s = np, odd np) has every key masked.
   auto step = [&](u32x4_t (&k)[NC], int s) {
     const int k0 = (pbeg + s) * kPage;  // first key of the page
     const bool inside = s < np;
@@ -284,7 +288,7 @@ __device__ __forceinline__ void decode_piece_keqv(const AttnArgs& a,
 #pragma unroll
       for (int c = 0; c < NC; ++c) *(u32x4_t*)(row_lds + 32 * c) = u32x4_t{0u, 0u, 0u, 0u};
     }
-    issue(k, s + 2 < np ? s + 2 : (s < np ? s : np - 1));
+    issue(k, s + 2 < np ? s + 2 : (s < np ? s : np - 1), s + 2 < np);
 
     float x[4];
     uint32_t pw[2];
@@ -310,8 +314,8 @@ __device__ __forceinline__ void decode_piece_keqv(const AttnArgs& a,
 
   if (np <= 0) return;
   u32x4_t kA[NC], kB[NC];
-  issue(kA, 0);
-  issue(kB, np > 1 ? 1 : 0);
+  issue(kA, 0, true);
+  issue(kB, np > 1 ? 1 : 0, np > 1);
   for (int s = 0; s < np; s += 2) {
     step(kA, s);
     step(kB, s + 1);
