@@ -275,8 +275,6 @@ prefill_tiled_kernel(AttnArgs a, int runs_per_bg, int n_groups) {
   const int last_page = (L - 1) / kPage;
   // exact K=V: this thread's unit pair in the rotation pass (row, unit column, page, tile of
   // the iteration)
-  const int rp_r = threadIdx.x & 15, rp_x = (threadIdx.x >> 4) & 7;
-  const int rp_p = (threadIdx.x >> 7) & 1, rp_u = threadIdx.x >> 8;
 
   // Lane offsets inside a tile (bytes); fragment c / column block nn adds an immediate.
   //   K, product m: row qk_row_key(c16, m) of page c16 / 8, chunk 4c + j.
@@ -559,6 +557,13 @@ prefill_tiled_kernel(AttnArgs a, int runs_per_bg, int n_groups) {
       // the rotated rope units of this iteration's tiles (the previous iteration's readers of
       // the buffer have all passed the barrier above)
       static_assert(TB == 2, "one rope buffer per tile of an iteration");
+      // this thread's unit pair (row, unit column, page, tile of the iteration), derived here
+      // from an opaque copy of the thread id so that nothing of the pass stays live across
+      // the key loop (held there, its values spilled)
+      int tid = (int)threadIdx.x;
+      asm volatile("" : "+v"(tid));
+      const int rp_r = tid & 15, rp_x = (tid >> 4) & 7;
+      const int rp_p = (tid >> 7) & 1, rp_u = tid >> 8;
       const int tl = TB * jj + rp_u;
       if (tl < np) {
         // source units rp_x and rp_x + D/16 of the K tile; in the rope buffer they become
