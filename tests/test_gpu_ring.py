@@ -117,3 +117,57 @@ def test_ring_write_matches_the_oracle_ring_write():
         assert ulp_distance(wl.to_numpy_bits(qd), qh).max() <= 1, step
         done += n
         step += 1
+
+
+def _draw_ring_case(rng):
+    dtype = "fp32" if rng.random() < 0.2 else "bf16"
+    D = int(rng.choice([128, 256, 512]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    W = int(rng.choice([1, 15, 16, 17, 31, 32, 33, 64, 100])) if rng.random() < 0.7 \
+        else int(rng.integers(2, 400))
+    B = int(rng.integers(1, 5))
+    lens = [int(rng.integers(1, 1600)) for _ in range(B)]
+    chunk = max(int(rng.integers(1, 2 * W + 48)), -(-max(lens) // 12))  # at most 12 chunks
+    return dict(dtype=dtype, D=D, Hq=G * Hkv, Hkv=Hkv, W=W, cap=float(rng.choice([0.0, 30.0])),
+                keqv=bool(rng.random() < 0.3), lens=lens, chunk=chunk)
+
+
+@pytest.mark.parametrize("block", range(2))
+def test_seeded_ring_fuzz(block):
+    """Seeded ring-table cases (seeds 9700 + 6 block ..): random shapes, windows, chunk sizes
+    and lengths, each through the smallest ring the library accepts for its chunk.  Every
+    chunk's prefill and the final decode equal the plain table's bit for bit; the last chunk
+    matches the oracle's ring path.  Every case is printed before it runs."""
+    rng = np.random.default_rng(9700 + block)
+    for i in range(6):
+        c = _draw_ring_case(rng)
+        seed = 9700 + 6 * block + i
+        print(f"ring fuzz case {seed}: {c}", flush=True)
+        spec = wl.LayerSpec(c["dtype"], c["Hq"], c["Hkv"], c["D"], window=c["W"], scale=1.0,
+                            softcap=c["cap"], k_eq_v=c["keqv"],
+                            rope_theta=1e4 if c["D"] < 512 else 1e6)
+        lens, chunk = c["lens"], c["chunk"]
+        ring = (chunk + c["W"] - 2) // 16 + 3
+        plain, ringc = _pair(spec, lens, ring, seed=seed)
+        done = np.zeros(len(lens), np.int64)
+        step = 0
+        while (done < lens).any():
+            n, cl = _chunks(lens, done, chunk)
+            cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+            outs = []
+            for case in (plain, ringc):
+                _, _, _, qd, _, _ = case.write(cl, n, seed * 100 + step)
+                outs.append((qd, case.prefill(qd, cu, cl, max_q_len=chunk)))
+            torch.cuda.synchronize()
+            assert torch.equal(outs[0][1], outs[1][1]), \
+                f"ring fuzz case {seed} chunk {step}: ring and plain disagree"
+            done += n
+            step += 1
+        kc, vc = ringc.host_caches()
+        ref = ringc.oracle_attention(outs[1][0], cu, cl, caches=(kc, vc))
+        assert_attn_close(outs[1][1], ref, c["dtype"], what=f"ring fuzz case {seed}, last chunk")
+        qdec = wl.raw_qkv(spec, len(lens), seed + 1)[0].to(ringc.dev)  # one query per sequence
+        dec = [case.decode(qdec, cl) for case in (plain, ringc)]
+        torch.cuda.synchronize()
+        assert torch.equal(dec[0], dec[1]), f"ring fuzz case {seed}: decode disagrees"
