@@ -447,7 +447,7 @@ def capture_chain(step_fn, n):
     """One HIP graph holding n consecutive steps step_fn(0) .. step_fn(n - 1).  A serving loop
     replays one graph per decode iteration over all its layers, so a graph launch is paid once
     per many layer steps; timing each step as its own graph would add a launch gap (about
-    8 us on the box) to every step."""
+    8 us on MI355X) to every step."""
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(n):
