@@ -64,7 +64,7 @@ def test_named_workloads_keep_their_size():
 
 
 @pytest.mark.parametrize("workload", [bench.HEADLINE, "sliding_decode_bf16",
-                                      "softcap_decode_bf16"])
+                                      "softcap_decode_bf16", bench.HEADLINE + "_exact"])
 def test_traffic_records_match_the_decode_sources(workload):
     """The counter records that the roofline blocks' traffic reads were taken on the current
     decode sources (bench.py reports null otherwise)."""
