@@ -426,8 +426,30 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(AttnArgs a) {
       decode_piece_kv<D, CAP>(a, qf, acc, b, g, L, lo, p0 + lp, p0 + lp + cnt);
     acc.l += __shfl_xor(acc.l, 16, kWave);
     acc.l += __shfl_xor(acc.l, 32, kWave);
-    const int64_t row = ((int64_t)worker + (int64_t)b * Hkv + g) * G + c16;
-    if (head_ok) {
+    if (lp == 0 && cnt == npg) {
+      // the worker holds the whole segment, so it writes the output itself (the merge skips
+      // the segments of one piece), by the merge's arithmetic for a single piece: o times
+      // 1 / l (and, exact K=V, times w_v / w_k)
+      if (head_ok) {
+        const float inv = 1.0f / acc.l;
+        uint16_t* dst = a.out + ((int64_t)b * a.Hq + g * G + c16) * D + 4 * j;
+#pragma unroll
+        for (int n = 0; n < D / 16; ++n) {
+          float f[4] = {inv, inv, inv, inv};
+          if constexpr (EXACT) {
+            if (a.kv_vw) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                f[i] *= a.kv_vw[16 * n + 4 * j + i] / a.kv_kw[16 * n + 4 * j + i];
+            }
+          }
+          *(u32x2_t*)(dst + 16 * n) =
+              u32x2_t{pack_bf16x2(acc.o[n][0] * f[0], acc.o[n][1] * f[1]),
+                      pack_bf16x2(acc.o[n][2] * f[2], acc.o[n][3] * f[3])};
+        }
+      }
+    } else if (head_ok) {
+      const int64_t row = ((int64_t)worker + (int64_t)b * Hkv + g) * G + c16;
 #pragma unroll
       for (int n = 0; n < D / 16; ++n) *(float4_t*)(a.ws_o + row * D + 16 * n + 4 * j) = acc.o[n];
       if (j == 0) *(float2*)(a.ws_ml + row * 2) = make_float2(acc.m, acc.l);
@@ -479,6 +501,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
   const int64_t start = pref_b * a.Hkv + (int64_t)g * npg;
   const int64_t w0 = start / per, w1 = (start + npg - 1) / per;
   const int ns = (int)(w1 - w0 + 1);
+  if (ns == 1) return;  // one worker held the whole segment and wrote the output
   const int64_t row0 = (w0 + (int64_t)b * a.Hkv + g) * G + hh;  // row of piece i: row0 + i*G
   const int c = t % C4, gi = t / C4;
   const float* ocol = a.ws_o + row0 * D + 4 * c;
