@@ -62,6 +62,23 @@ def test_decode_batch_sizes_around_one_wave(B, D, Hq, Hkv, W):
     assert_attn_close(out, ref, "bf16", what=f"decode B{B} D{D} W{W}")
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,D,W,keqv,maxlen", [
+    (64, 32, 16, 256, 0, False, 3000),
+    (64, 32, 4, 512, 0, True, 2000),
+    (128, 16, 16, 128, 100, False, 400),
+])
+def test_decode_many_outputs(B, Hq, Hkv, D, W, keqv, maxlen):
+    """Batches of 2048 or more (sequence, query head) outputs whose ragged lengths give both
+    segments held whole by one worker (the worker writes the output and the merge skips
+    them) and segments split over two to ten workers, side by side in one call."""
+    spec = wl.LayerSpec("bf16", Hq, Hkv, D, window=W, k_eq_v=keqv,
+                        rope_theta=1e4 if D < 512 else 1e6)
+    g = np.random.default_rng(200 + D)
+    lens = [int(x) for x in g.integers(1, maxlen, size=B)]
+    out, ref = _decode_case(spec, lens, seed=24 + D)
+    assert_attn_close(out, ref, "bf16", what=f"decode B{B} Hq{Hq} D{D}")
+
+
 def test_decode_softcap_binds():
     """q scaled by 20 so that the cap of 50 dominates the scores."""
     spec = wl.LayerSpec("bf16", 8, 4, 256, softcap=50.0, scale=1 / 16, norm_q=False,
