@@ -79,24 +79,19 @@ __device__ __forceinline__ int qk_row_key(int c16, int m) {
   return (c16 & 3) + 8 * ((c16 >> 2) & 1) + 4 * m;
 }
 
-// One HBM -> LDS copy of 1 KiB: each lane moves 16 bytes to M0 + 16 * lane.  Issued through
+// One HBM -> LDS copy of 1 KiB from a wave-uniform 64-bit base (scalar registers) plus a
+// 32-bit per-lane byte offset: each lane moves 16 bytes to M0 + 16 * lane.  Issued through
 // inline assembly so that the compiler does not add waits of its own for the LDS it writes:
-// the kernel waits on the vector-memory counter explicitly before the barrier that
-// publishes a tile.  No memory clobber: a copy only ever writes a ring stage that no LDS
-// access of the same iteration touches, and being volatile it stays ordered with the
-// barriers and explicit waits that separate iterations.
-__device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds_off) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(lds_off)
-               : "m0");
-}
-
-// The same copy from a wave-uniform 64-bit base (scalar registers) plus a 32-bit per-lane
-// byte offset: a lane then needs one vector register per copy pattern instead of a 64-bit
-// address per copy, and the base is formed by scalar arithmetic.
+// the kernel waits on the vector-memory counter explicitly before the barrier that publishes
+// a tile.  No memory clobber: a copy only ever writes a ring stage that no LDS access of the
+// same iteration touches, and being volatile it stays ordered with the barriers and explicit
+// waits that separate iterations.  An LDS DMA must not issue in the instruction right after
+// a scalar write of M0 (one wait state; the compiler pads its own such pairs with s_nop 0),
+// hence the nop.  M0 is set inside the statement each time: nothing in these kernels leaves
+// a value of the compiler's own in M0 (on this target it uses M0 for LDS DMA, messages and
+// indirect register indexing, which the kernels do not ask of it).
 __device__ __forceinline__ void lds_copy16_sv(const void* base, uint32_t voff, uint32_t lds_off) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(base), "s"(lds_off)
                : "m0");
