@@ -97,20 +97,6 @@ __device__ __forceinline__ void lds_copy16_sv(const void* base, uint32_t voff, u
                : "m0");
 }
 
-// Two consecutive int32 (wave-uniform address) through the scalar cache, waited for inside the
-// same statement so the value is complete when the statement ends.  Used only where no LDS
-// read of this wave is outstanding (the wait covers those too).
-__device__ __forceinline__ int2 scalar_load2(const int32_t* p) {
-  int2 v;
-  asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
-  return v;
-}
-__device__ __forceinline__ int scalar_load1(const int32_t* p) {
-  int v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
-  return v;
-}
-
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
