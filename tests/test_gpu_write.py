@@ -227,3 +227,44 @@ def test_kv_sharing_topology_sliding_and_global_sources():
                                  float(np.float32(spec.softcap)), int(spec.k_eq_v),
                                  wl.to_numpy_bits(qd), kc, vc, pb.block_table, cl)
         assert_attn_close(out, ref, "bf16", what=f"shared layer {i} ({which})")
+
+
+def _draw_write_case(rng):
+    dtype = "fp32" if rng.random() < 0.2 else "bf16"
+    D = int(rng.choice([128, 256, 512]))
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    theta = 0.0 if rng.random() < 0.1 else float(rng.choice([1e4, 1e6]))
+    angles = int(rng.choice([0, 1, 8, 20, D // 4, D // 2]))
+    scale_f = float(rng.choice([0.0, 0.0, 4.0, 8.0]))
+    norms = [bool(rng.random() < 0.8) for _ in range(3)]
+    keqv = bool(rng.random() < 0.3)
+    B = int(rng.integers(1, 7))
+    lens = [int(x) for x in rng.integers(1, 3000, size=B)]
+    if rng.random() < 0.5:  # a decode step: one new token per sequence
+        news = [1] * B
+    else:                   # chunks, one of them possibly the whole sequence
+        news = [int(rng.integers(1, min(L, 600) + 1)) for L in lens]
+    return dict(dtype=dtype, D=D, Hq=G * Hkv, Hkv=Hkv, theta=theta, angles=angles, f=scale_f,
+                norms=norms, keqv=keqv, lens=lens, news=news)
+
+
+@pytest.mark.parametrize("block", range(2))
+def test_seeded_write_fuzz(block):
+    """Seeded write cases (seeds 9800 + 8 block ..): random head sizes, group sizes, dtypes,
+    RoPE bases, rotated-pair counts, linear factors, norms on or off, K=V, and ragged batches
+    written as a decode step or as chunks after a cached past.  Every stored key and value
+    and the returned q within 1 ulp of the oracle's write (bit-exact where nothing is
+    normalised or rotated).  Every case is printed before it runs."""
+    rng = np.random.default_rng(9800 + block)
+    for i in range(8):
+        c = _draw_write_case(rng)
+        seed = 9800 + 8 * block + i
+        print(f"write fuzz case {seed}: {c}", flush=True)
+        spec = wl.LayerSpec(c["dtype"], c["Hq"], c["Hkv"], c["D"], rope_theta=c["theta"],
+                            rope_angles=c["angles"], rope_scale=c["f"], k_eq_v=c["keqv"],
+                            norm_q=c["norms"][0], norm_k=c["norms"][1], norm_v=c["norms"][2])
+        dk, dv, dq = _run(spec, c["lens"], c["news"], seed=seed)
+        for name, d in (("k", dk), ("v", dv), ("q", dq)):
+            if d is not None:
+                assert d.max() <= 1, f"write fuzz case {seed}: {name} differs by {d.max()} ulp"
